@@ -1,0 +1,65 @@
+"""Pins of the bfloat16 / e4m3fn decoding and of the 656-byte FP8 record
+against closed forms, the pages' figures and torch's own conversions."""
+
+import numpy as np
+import torch
+
+from oracle import numerics as Nm
+from oracle import fp8cache as F8
+from workloads.gen import encode_fp8_records
+
+
+def test_e4m3_all_codes_closed_form_and_library():
+    codes = np.arange(256, dtype=np.uint8)
+    got = Nm.e4m3fn_decode(codes)
+    lib = torch.from_numpy(codes.copy()).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    for c in range(256):
+        s = -1.0 if c & 0x80 else 1.0
+        e, m = (c >> 3) & 15, c & 7
+        if e == 15 and m == 7:
+            assert np.isnan(got[c]) and np.isnan(lib[c])
+            continue
+        ref = s * (2.0 ** -6) * (m / 8) if e == 0 else s * 2.0 ** (e - 7) * (1 + m / 8)
+        assert got[c] == ref == lib[c]
+    finite = got[np.isfinite(got)]
+    assert finite.size == 254 and finite.max() == 448.0
+
+
+def test_bf16_bits_roundtrip_and_rne_against_torch():
+    rng = np.random.default_rng(0)
+    x = rng.standard_normal(100000).astype(np.float32) * np.float32(3.0)
+    # exact ties: bf16 value + half an ulp
+    base = torch.from_numpy(x[:2000]).to(torch.bfloat16).to(torch.float32).numpy()
+    ties = (base.view(np.uint32) | np.uint32(0x8000)).view(np.float32)
+    special = np.array([0.0, -0.0, np.inf, -np.inf, 3.3895314e38, 1e-40, -1e-45], dtype=np.float32)
+    allx = np.concatenate([x, ties, special])
+    ours = Nm.f32_to_bf16_bits_rne(allx)
+    lib = torch.from_numpy(allx).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(ours, lib)
+    back = Nm.bf16_bits_to_f64(ours)
+    assert np.array_equal(back, torch.from_numpy(allx).to(torch.bfloat16).to(torch.float64).numpy())
+
+
+def test_record_layout_matches_pages(golden):
+    g = golden['fp8_record_bytes']
+    assert F8.RECORD_BYTES == g['value'] == sum(g['parts'])
+    assert list(F8.record_layout()) == g['parts']
+
+
+def test_dequant_against_torch_conversions():
+    gen = torch.Generator().manual_seed(3)
+    x = torch.randn(300, 576, generator=gen)
+    x[5, :128] = 0.0                       # an all-zero tile (scale 1)
+    x[6, 7] = 1e-9                         # subnormal region
+    rec = encode_fp8_records(x[:, :512].contiguous(), x[:, 512:].to(torch.bfloat16))
+    got = F8.dequant_records(rec.numpy())
+    codes = rec[:, :512].contiguous().view(torch.float8_e4m3fn).to(torch.float32)
+    scales = rec[:, 512:528].contiguous().view(torch.float32)
+    ref_lat = (codes.view(300, 4, 128) * scales[:, :, None]).view(300, 512).to(torch.bfloat16)
+    ref_rope = rec[:, 528:].contiguous().view(torch.bfloat16)
+    ref = torch.cat([ref_lat, ref_rope], dim=1).to(torch.float64).numpy()
+    assert np.array_equal(got, ref)
+    # dequantised values approximate the source within e4m3 resolution
+    err = np.abs(got[:, :512] - x[:, :512].numpy())
+    amax = np.abs(x[:, :512].numpy()).reshape(300, 4, 128).max(axis=2)
+    assert np.all(err.reshape(300, 4, 128) <= (amax / 448.0 * 16.0 + amax * 2.0 ** -8 + 1e-6)[:, :, None])

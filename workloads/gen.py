@@ -1,0 +1,239 @@
+"""Seeded synthetic workloads with the shapes of the pages' decode settings.
+
+Recipe (all values from torch generators seeded per workload):
+* q and bfloat16 cache rows: N(0, 1) in float32, rounded to bfloat16;
+* paged caches: 64-token pages drawn from a shuffled pool (``randperm``), so
+  consecutive logical pages of a request sit at random physical places; table
+  slots past a request's last page are 0 and never read;
+* DSA top-k: per query token, ``topk`` distinct logical tokens of the request,
+  encoded as page_block*64 + offset through the request's block table; each
+  slot is set to -1 with probability ``invalid_frac``;
+* peaked top-k rows: slot 0 holds the query's own (newest) token r and
+  q[b, 0, h] = 0.25 * k_r for every head (exact in bfloat16);
+* FP8 cache: per token, N(0, 1) latent values quantised per 1x128 tile with
+  scale = amax / 448 and float8_e4m3fn codes (torch's round-to-nearest cast
+  after clamping to +-448); RoPE values N(0, 1) rounded to bfloat16; record =
+  [512 codes | 4 float32 scales | 64 bfloat16], little-endian.
+
+Large tensors are drawn on ``device`` with a generator for that device, so the
+values depend on the device the workload is built for; index structures are
+always drawn on the CPU.
+"""
+
+from dataclasses import dataclass, field
+from typing import Optional
+import math
+
+import torch
+
+D_QK = 576
+D_V = 512
+BLOCK = 64
+FP8_RECORD = 656
+
+CONFIG_NAMES = {
+    1: 'tiny dense b=2 s_q=1 h_q=16 L={200,256} fp32 out',
+    2: 'DeepSeek-V3 dense b=64 s_q=1 h_q=128 L=4096',
+    3: 'var-len spec decode b=128 s_q=2 causal h_q=128 L~U[1,8192]',
+    4: 'sparse top-k b=64 s_q=1 h_q=128 topk=2048 pool 32768/seq 5% invalid',
+    5: 'FP8 cache b=32 s_q=1 h_q=128 L=16384',
+}
+
+
+@dataclass
+class Workload:
+    name: str
+    batch: int
+    s_q: int
+    h_q: int
+    causal: bool
+    topk: int                       # 0 = dense
+    kv_format: str                  # 'bf16' | 'fp8'
+    out_dtype: str                  # 'bf16' | 'fp32'
+    softmax_scale: float
+    q: torch.Tensor                 # bf16 [B, S, H, 576]
+    kv: torch.Tensor                # bf16 [NB, 64, 1, 576] or uint8 [NB, 64, 1, 656]
+    block_table: torch.Tensor       # int32 [B, max_blocks]
+    cache_seqlens: torch.Tensor     # int32 [B]
+    indices: Optional[torch.Tensor] = None   # int32 [B, S, topk]
+    meta: dict = field(default_factory=dict)
+
+    @property
+    def num_blocks(self):
+        return int(self.kv.shape[0])
+
+    @property
+    def max_blocks_per_seq(self):
+        return int(self.block_table.shape[1])
+
+    def to(self, device):
+        kw = {}
+        for k in ('q', 'kv', 'block_table', 'cache_seqlens', 'indices'):
+            v = getattr(self, k)
+            kw[k] = None if v is None else v.to(device)
+        return Workload(self.name, self.batch, self.s_q, self.h_q, self.causal, self.topk,
+                        self.kv_format, self.out_dtype, self.softmax_scale, meta=dict(self.meta), **kw)
+
+
+def _gen(device, seed):
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    return g
+
+
+def _randn_bf16(shape, g, device, chunk_rows=4096):
+    """N(0,1) float32 rounded to bfloat16, drawn in chunks along dim 0."""
+    out = torch.empty(shape, dtype=torch.bfloat16, device=device)
+    n0 = shape[0]
+    for s in range(0, n0, chunk_rows):
+        e = min(n0, s + chunk_rows)
+        out[s:e] = torch.randn((e - s,) + tuple(shape[1:]), generator=g, device=device).to(torch.bfloat16)
+    return out
+
+
+def _paged_table(seqlens, max_blocks, g_cpu, pool_blocks=None):
+    """Shuffled pool of pages; returns (num_blocks, table int32 [B, max_blocks])."""
+    need = [max(1, math.ceil(int(L) / BLOCK)) if int(L) > 0 else 0 for L in seqlens]
+    total = sum(need)
+    nb = total if pool_blocks is None else int(pool_blocks)
+    assert nb >= total
+    perm = torch.randperm(nb, generator=g_cpu)
+    table = torch.zeros((len(seqlens), max_blocks), dtype=torch.int32)
+    o = 0
+    for b, k in enumerate(need):
+        assert k <= max_blocks
+        table[b, :k] = perm[o:o + k].to(torch.int32)
+        o += k
+    return nb, table
+
+
+def make_dense(batch, s_q, h_q, seqlens, *, causal=False, seed=0, device='cpu', out_dtype='bf16',
+               max_blocks=None, pool_blocks=None, softmax_scale=None, name='dense'):
+    g_cpu = _gen('cpu', seed)
+    seqlens = [int(x) for x in seqlens]
+    assert len(seqlens) == batch
+    if max_blocks is None:
+        max_blocks = max(1, max(math.ceil(L / BLOCK) for L in seqlens))
+    nb, table = _paged_table(seqlens, max_blocks, g_cpu, pool_blocks)
+    g = _gen(device, seed + 7919)
+    q = _randn_bf16((batch, s_q, h_q, D_QK), g, device, chunk_rows=64)
+    kv = _randn_bf16((max(nb, 1), BLOCK, 1, D_QK), g, device, chunk_rows=1024)
+    return Workload(name, batch, s_q, h_q, causal, 0, 'bf16', out_dtype,
+                    softmax_scale if softmax_scale is not None else 1.0 / math.sqrt(D_QK),
+                    q, kv, table.to(device), torch.tensor(seqlens, dtype=torch.int32, device=device))
+
+
+def encode_fp8_records(x, rope_bf16):
+    """x float32 [n, 512], rope bf16 [n, 64] -> uint8 records [n, 656]."""
+    n = x.shape[0]
+    tiles = x.view(n, 4, 128)
+    amax = tiles.abs().amax(dim=2)
+    scale = torch.where(amax > 0, amax / 448.0, torch.ones_like(amax)).to(torch.float32)
+    codes = (tiles / scale[:, :, None]).clamp(-448.0, 448.0).to(torch.float8_e4m3fn).view(n, 512)
+    rec = torch.empty((n, FP8_RECORD), dtype=torch.uint8, device=x.device)
+    rec[:, :512] = codes.view(torch.uint8)
+    rec[:, 512:528] = scale.contiguous().view(torch.uint8).view(n, 16)
+    rec[:, 528:] = rope_bf16.contiguous().view(torch.uint8).view(n, 128)
+    return rec
+
+
+def make_fp8_dense(batch, s_q, h_q, seqlens, *, causal=False, seed=0, device='cpu', out_dtype='bf16',
+                   max_blocks=None, pool_blocks=None, softmax_scale=None, name='fp8'):
+    g_cpu = _gen('cpu', seed)
+    seqlens = [int(x) for x in seqlens]
+    if max_blocks is None:
+        max_blocks = max(1, max(math.ceil(L / BLOCK) for L in seqlens))
+    nb, table = _paged_table(seqlens, max_blocks, g_cpu, pool_blocks)
+    g = _gen(device, seed + 7919)
+    q = _randn_bf16((batch, s_q, h_q, D_QK), g, device, chunk_rows=64)
+    nb = max(nb, 1)
+    kv = torch.empty((nb, BLOCK, 1, FP8_RECORD), dtype=torch.uint8, device=device)
+    step = 256
+    for s in range(0, nb, step):
+        e = min(nb, s + step)
+        n = (e - s) * BLOCK
+        x = torch.randn((n, D_QK), generator=g, device=device)
+        rec = encode_fp8_records(x[:, :512].contiguous(), x[:, 512:].to(torch.bfloat16))
+        kv[s:e] = rec.view(e - s, BLOCK, 1, FP8_RECORD)
+    return Workload(name, batch, s_q, h_q, causal, 0, 'fp8', out_dtype,
+                    softmax_scale if softmax_scale is not None else 1.0 / math.sqrt(D_QK),
+                    q, kv, table.to(device), torch.tensor(seqlens, dtype=torch.int32, device=device))
+
+
+def make_sparse(batch, s_q, h_q, *, pool_tokens_per_seq, topk, invalid_frac=0.05, seed=0, device='cpu',
+                out_dtype='bf16', peaked=False, order='asis', softmax_scale=None, kv_format='bf16',
+                name='sparse'):
+    """DSA-style top-k decode inputs.  ``order``: 'asis' | 'self_last' | 'perm'."""
+    g_cpu = _gen('cpu', seed)
+    blocks_per_seq = math.ceil(pool_tokens_per_seq / BLOCK)
+    seqlens = [pool_tokens_per_seq] * batch
+    nb, table = _paged_table(seqlens, blocks_per_seq, g_cpu)
+    n_tok = pool_tokens_per_seq
+    assert topk <= n_tok
+    idx = torch.empty((batch, s_q, topk), dtype=torch.int64)
+    for b in range(batch):
+        for i in range(s_q):
+            if peaked:
+                self_tok = n_tok - s_q + i
+                rest = torch.randperm(n_tok - 1, generator=g_cpu)[:topk - 1]
+                rest = torch.where(rest >= self_tok, rest + 1, rest)
+                sel = torch.cat([torch.tensor([self_tok]), rest])
+            else:
+                sel = torch.randperm(n_tok, generator=g_cpu)[:topk]
+            phys = table[b].to(torch.int64)[sel // BLOCK] * BLOCK + sel % BLOCK
+            drop = torch.rand(topk, generator=g_cpu) < invalid_frac
+            if peaked:
+                drop[0] = False
+            phys = torch.where(drop, torch.full_like(phys, -1), phys)
+            if order == 'self_last':
+                phys = torch.roll(phys, -1)
+            elif order == 'perm':
+                phys = phys[torch.randperm(topk, generator=g_cpu)]
+            idx[b, i] = phys
+    g = _gen(device, seed + 7919)
+    if kv_format == 'bf16':
+        kv = _randn_bf16((nb, BLOCK, 1, D_QK), g, device, chunk_rows=1024)
+    else:
+        kv = torch.empty((nb, BLOCK, 1, FP8_RECORD), dtype=torch.uint8, device=device)
+        for s in range(0, nb, 256):
+            e = min(nb, s + 256)
+            x = torch.randn(((e - s) * BLOCK, D_QK), generator=g, device=device)
+            kv[s:e] = encode_fp8_records(x[:, :512].contiguous(),
+                                         x[:, 512:].to(torch.bfloat16)).view(e - s, BLOCK, 1, FP8_RECORD)
+    q = _randn_bf16((batch, s_q, h_q, D_QK), g, device, chunk_rows=64)
+    indices = idx.to(torch.int32).to(device)
+    if peaked:
+        assert kv_format == 'bf16'
+        flat = kv.view(-1, D_QK)
+        for b in range(batch):
+            for i in range(s_q):
+                self_tok = n_tok - s_q + i
+                r = int(table[b, self_tok // BLOCK]) * BLOCK + self_tok % BLOCK
+                q[b, i, :, :] = (flat[r].to(torch.float32) * 0.25).to(torch.bfloat16)[None, :]
+    return Workload(name, batch, s_q, h_q, False, topk, kv_format, out_dtype,
+                    softmax_scale if softmax_scale is not None else 1.0 / math.sqrt(D_QK),
+                    q, kv, table.to(device), torch.tensor(seqlens, dtype=torch.int32, device=device),
+                    indices=indices, meta={'peaked': peaked, 'order': order})
+
+
+def make_config(i, device='cpu', seed=None, **kw):
+    """The five workloads, with seed 1000 + i unless given."""
+    seed = 1000 + i if seed is None else seed
+    if i == 1:
+        return make_dense(2, 1, 16, [200, 256], seed=seed, device=device, out_dtype='fp32',
+                          max_blocks=4, pool_blocks=8, name='config1', **kw)
+    if i == 2:
+        return make_dense(64, 1, 128, [4096] * 64, seed=seed, device=device, max_blocks=64,
+                          pool_blocks=4096, name='config2', **kw)
+    if i == 3:
+        g = _gen('cpu', seed + 17)
+        lens = torch.randint(1, 8193, (128,), generator=g).tolist()
+        return make_dense(128, 2, 128, lens, causal=True, seed=seed, device=device, max_blocks=128,
+                          name='config3', **kw)
+    if i == 4:
+        return make_sparse(64, 1, 128, pool_tokens_per_seq=32768, topk=2048, invalid_frac=0.05,
+                           seed=seed, device=device, name='config4', **kw)
+    if i == 5:
+        return make_fp8_dense(32, 1, 128, [16384] * 32, seed=seed, device=device, max_blocks=256,
+                              pool_blocks=8192, name='config5', **kw)
+    raise ValueError(i)
