@@ -1,0 +1,181 @@
+/*
+ * mla_decode.h -- C ABI of the MI355X (gfx950) absorbed-MLA decode library.
+ *
+ * The operation (FlashMLA new-kernel deep dive, "Theoretical analysis"; the
+ * "matrices, attention & GPU" explainer, sections 5-7; FlashMLA README,
+ * "Usage"): after the MLA up-projections are absorbed into the query and the
+ * output projection, decoding is multi-query attention.  Every query token
+ * has h_q heads of width d_qk = 576 (512 latent + 64 RoPE) and attends to one
+ * shared KV head read from a paged latent cache; K is all 576 dims of a cached
+ * row and V its first d_v = 512 dims:
+ *
+ *     out[b, i, h, :] = softmax_t(scale * q[b, i, h, :] . K_t) V_t
+ *     lse[b, h, i]    = ln sum_t exp(scale * q[b, i, h, :] . K_t)
+ *
+ * with t ranging over the visible cache tokens (dense: the first
+ * cache_seqlens[b] tokens through block_table, bottom-right causal when
+ * requested; sparse: the valid top-k indices).  A query that sees no token
+ * gets out = 0 and lse = -inf.
+ *
+ * Conventions for every entry point:
+ *  - Device pointers point to contiguous, row-major device memory owned by the
+ *    caller; the library allocates no device memory and keeps no state other
+ *    than a per-device cache of the compute-unit count.
+ *  - Work is enqueued on ``stream`` (a hipStream_t; NULL = the null stream) and
+ *    is asynchronous; device-side faults surface at the caller's next sync.
+ *  - Argument, shape and alignment errors are reported synchronously, before
+ *    anything is launched, by the returned status.  q, kv_cache, out,
+ *    workspace and the metadata buffer must be 16-byte aligned.
+ *  - Entry points are thread-safe; calls that share a workspace or metadata
+ *    buffer must be ordered by the caller (same stream or events).
+ */
+#ifndef MLA_DECODE_H
+#define MLA_DECODE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MLA_DECODE_ABI_VERSION 1
+
+typedef enum {
+    MLA_OK = 0,
+    MLA_ERR_INVALID_ARG = 1,          /* null/misaligned pointer, bad size or flag */
+    MLA_ERR_UNSUPPORTED = 2,          /* well-formed but outside the supported set */
+    MLA_ERR_WORKSPACE_TOO_SMALL = 3,  /* workspace_bytes < mla_workspace_bytes() */
+    MLA_ERR_METADATA_MISMATCH = 4,    /* metadata planned for another problem */
+    MLA_ERR_HIP = 5                   /* a HIP runtime call failed */
+} mla_status_t;
+
+typedef enum {
+    MLA_KV_BF16_576 = 0,  /* 576 bfloat16 per token (1152 B)                        */
+    MLA_KV_FP8_656 = 1    /* 512 e4m3fn | 4 float32 scales (1 per 128) | 64 bf16   */
+} mla_kv_format_t;
+
+typedef enum { MLA_OUT_BF16 = 0, MLA_OUT_FP32 = 1 } mla_out_dtype_t;
+
+/* Problem shape.  Supported: h_kv = 1, d_qk = 576, d_v = 512, block_size = 64
+ * (FlashMLA README: the key cache has one head; d_v can only be 512).  Tensor
+ * layouts:
+ *   q            [batch, s_q, h_q, 576]              bfloat16
+ *   kv_cache     [num_blocks, 64, 1, 576] bfloat16   or
+ *                [num_blocks, 64, 1, 656] uint8 (MLA_KV_FP8_656)
+ *   block_table  [batch, max_blocks_per_seq]         int32 page ids
+ *   cache_seqlens[batch]                             int32, in [0, 64*max_blocks_per_seq]
+ *   indices      [batch, s_q, topk]                  int32 page*64 + offset; -1 invalid
+ *   out          [batch, s_q, h_q, 512]              bfloat16 or float32
+ *   lse          [batch, h_q, s_q]                   float32 (natural log)
+ */
+typedef struct {
+    int32_t batch;
+    int32_t s_q;
+    int32_t h_q;
+    int32_t h_kv;
+    int32_t d_qk;
+    int32_t d_v;
+    int32_t block_size;
+    int32_t num_blocks;
+    int32_t max_blocks_per_seq;  /* dense: block_table columns; may be 0 for sparse */
+    int32_t topk;                /* 0 = dense decode; > 0 = top-k sparse decode     */
+    int32_t causal;              /* dense only: bottom-right causal over the s_q tokens */
+    int32_t kv_format;           /* mla_kv_format_t */
+    int32_t out_dtype;           /* mla_out_dtype_t */
+    float softmax_scale;         /* multiplies q . k before the softmax */
+} mla_problem_t;
+
+/* Split-KV schedule for one problem shape.  ``mla_plan`` fills everything
+ * except ``dev``; the caller allocates ``bytes`` of device memory for ``dev``
+ * and reuses the filled buffer for every call (every layer) of one decode
+ * step (FlashMLA README, "Usage": metadata is made once before the layer loop).
+ * Device layout of ``dev`` (int32): 8-word header, num_partitions records of 5
+ * words (begin_item, begin_tile, end_item, end_tile, first_split_slot), then
+ * split_offsets[batch*s_q + 1]. */
+typedef struct {
+    mla_problem_t sig;           /* problem the plan was made for */
+    int32_t num_partitions;      /* P: workgroup columns of the split-KV grid */
+    int32_t num_head_blocks;     /* ceil(h_q / 64) */
+    int32_t fixed_overhead;      /* F: per-item cost added by the scheduler */
+    int32_t max_splits;          /* upper bound of split slots: batch*s_q + P */
+    void *dev;                   /* caller-owned device buffer, >= bytes */
+    size_t bytes;                /* size of the device metadata */
+} mla_metadata_t;
+
+/* Library ABI version (MLA_DECODE_ABI_VERSION). */
+int32_t mla_abi_version(void);
+
+/* Human-readable name of a status code (static storage). */
+const char *mla_status_string(mla_status_t status);
+
+/* Validate ``problem`` and fill ``meta`` (all fields but ``dev``) for a device
+ * with ``num_cus`` compute units; num_cus = 0 queries the current device.
+ * Pure host computation when num_cus > 0.  Errors: INVALID_ARG for null
+ * pointers or impossible sizes, UNSUPPORTED for shapes outside the supported
+ * set, HIP if the device query fails. */
+mla_status_t mla_plan(const mla_problem_t *problem, int32_t num_cus, mla_metadata_t *meta);
+
+/* Bytes of the split-partial workspace a decode call with this plan needs:
+ * max_splits * h_q * (512 + 1) float32.  0 if ``meta`` is NULL. */
+size_t mla_workspace_bytes(const mla_metadata_t *meta);
+
+/* a1: split-KV tile scheduler.  Writes meta->dev on ``stream`` from
+ * cache_seqlens (device, [batch]; ignored and may be NULL when topk > 0).
+ * The scheduler balances KV tiles of 64 tokens (plus a fixed per-item cost)
+ * over the partitions in contiguous ranges (FlashMLA new-kernel deep dive,
+ * "Other performance improvements": the tile scheduler spreads requests and
+ * blocks evenly over the compute units).  Errors: INVALID_ARG, UNSUPPORTED,
+ * METADATA_MISMATCH if meta was planned for another problem, HIP. */
+mla_status_t mla_get_decode_metadata(const mla_problem_t *problem, const int32_t *cache_seqlens,
+                                     mla_metadata_t *meta, void *stream);
+
+/* a2-a9, dense: decode over the paged cache through block_table and
+ * cache_seqlens (both device).  problem->topk must be 0.  Writes out and lse.
+ * ``workspace`` holds split partials (device, >= mla_workspace_bytes(meta)).
+ * The caller keeps ``meta->dev`` current: reusing metadata made from other
+ * cache_seqlens silently mis-splits (the pages give the same warning).
+ * Errors: INVALID_ARG, UNSUPPORTED, WORKSPACE_TOO_SMALL, METADATA_MISMATCH, HIP. */
+mla_status_t mla_decode_fwd(const mla_problem_t *problem, const void *q, const void *kv_cache,
+                            const int32_t *block_table, const int32_t *cache_seqlens,
+                            const mla_metadata_t *meta, void *workspace, size_t workspace_bytes,
+                            void *out, float *lse, void *stream);
+
+/* a2-a9, top-k sparse (DeepSeek Sparse Attention): each query token attends
+ * to the cache rows listed in indices[b, i, :] (device int32, page*64 +
+ * offset; block_table is not used, FlashMLA README "indices Tensor").  Entries
+ * < 0 or >= num_blocks*64 are masked (the pages mark -1 invalid and do no
+ * upper-bound check; this library masks instead of faulting).  problem->topk
+ * must be > 0 and problem->causal 0.  Same errors as mla_decode_fwd. */
+mla_status_t mla_sparse_decode_fwd(const mla_problem_t *problem, const void *q, const void *kv_cache,
+                                   const int32_t *indices, const mla_metadata_t *meta,
+                                   void *workspace, size_t workspace_bytes,
+                                   void *out, float *lse, void *stream);
+
+/* a9: LSE merge of split partials ("matrices, attention & GPU" explainer,
+ * split-KV section: m = max(m1, m2), l = l1 e^(m1-m) + l2 e^(m2-m),
+ * o = (o1 l1 e^(m1-m) + o2 l2 e^(m2-m)) / l).  Item j = b*s_q + i owns the
+ * split slots [split_offsets[j], split_offsets[j+1]) of
+ *   o_part   [slots, h_q, 512] float32 (normalised partial outputs)
+ *   lse_part [slots, h_q]      float32 (natural-log lse, -inf = empty)
+ * and receives out[b, i, :, :] and lse[b, :, i].  An item with no slot, or
+ * whose partials are all -inf, gets out = 0 and lse = -inf.  All pointers are
+ * device memory.  Errors: INVALID_ARG, HIP. */
+mla_status_t mla_combine(int32_t num_items, int32_t h_q, int32_t s_q, const float *o_part,
+                         const float *lse_part, const int32_t *split_offsets, int32_t out_dtype,
+                         void *out, float *lse, void *stream);
+
+/* Test hook for a2: writes, for every item j and KV slot t < tiles_j*64, the
+ * physical cache row the decode kernels read for that slot, or -1 where the
+ * slot is masked; rows_out is device int32 [batch*s_q, row_stride] with
+ * row_stride = 64*max_blocks_per_seq (dense) or 64*ceil(topk/64) (sparse);
+ * columns past an item's tiles are left untouched.  ``table_or_indices`` is
+ * block_table (dense) or indices (sparse).  Errors: INVALID_ARG, UNSUPPORTED, HIP. */
+mla_status_t mla_debug_gather_rows(const mla_problem_t *problem, const int32_t *table_or_indices,
+                                   const int32_t *cache_seqlens, int32_t *rows_out, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MLA_DECODE_H */

@@ -1,0 +1,176 @@
+"""Absorbed-MLA decoding for MI355X (gfx950): thin Python binding.
+
+The functions mirror the C entry points in ``include/mla_decode.h``
+(``mla_get_decode_metadata``, ``mla_decode_fwd``, ``mla_sparse_decode_fwd``,
+``mla_combine``, ...).  PyTorch only supplies device memory and the current
+stream; each call checks tensor placement, dtype and contiguity, passes raw
+pointers, and raises ``MlaError`` on a non-OK status.  All compute runs in the
+HIP library; if it is not built, importing the binding's functions raises.
+"""
+
+import ctypes
+import math
+
+import torch
+
+from . import _lib
+from ._lib import MlaError, Problem, Metadata  # noqa: F401
+
+__all__ = ["make_problem", "plan", "workspace_bytes", "get_decode_metadata", "decode_fwd",
+           "sparse_decode_fwd", "combine", "debug_gather_rows", "Decoder", "MlaError", "abi_version"]
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else None
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _need(t, name, dtype, device=None):
+    if t is None:
+        raise ValueError(f"{name} is required")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
+def abi_version():
+    return _lib.load().mla_abi_version()
+
+
+def make_problem(batch, s_q, h_q, num_blocks, max_blocks_per_seq=0, *, topk=0, causal=False, kv_format="bf16",
+                 out_dtype="bf16", softmax_scale=None):
+    p = Problem()
+    p.batch, p.s_q, p.h_q, p.h_kv, p.d_qk, p.d_v, p.block_size = batch, s_q, h_q, 1, 576, 512, 64
+    p.num_blocks, p.max_blocks_per_seq, p.topk, p.causal = num_blocks, max_blocks_per_seq, topk, int(bool(causal))
+    p.kv_format = {"bf16": _lib.KV_BF16_576, "fp8": _lib.KV_FP8_656}[kv_format]
+    p.out_dtype = {"bf16": _lib.OUT_BF16, "fp32": _lib.OUT_FP32}[out_dtype]
+    p.softmax_scale = 1.0 / math.sqrt(576) if softmax_scale is None else float(softmax_scale)
+    return p
+
+
+def plan(problem, num_cus=0):
+    """Host-side plan (mla_plan): partitions, head blocks, metadata and workspace sizes."""
+    lib = _lib.load()
+    m = Metadata()
+    _lib.check("mla_plan", lib.mla_plan(ctypes.byref(problem), int(num_cus), ctypes.byref(m)))
+    return m
+
+
+def workspace_bytes(meta):
+    return int(_lib.load().mla_workspace_bytes(ctypes.byref(meta)))
+
+
+def get_decode_metadata(problem, cache_seqlens, meta, meta_buf, stream=None):
+    """a1: fill ``meta_buf`` (device uint8/int32 tensor >= meta.bytes) with the schedule."""
+    lib = _lib.load()
+    _need(meta_buf, "meta_buf", None)
+    if meta_buf.numel() * meta_buf.element_size() < meta.bytes:
+        raise ValueError("meta_buf too small")
+    if cache_seqlens is not None:
+        _need(cache_seqlens, "cache_seqlens", torch.int32)
+    meta.dev = meta_buf.data_ptr()
+    _lib.check("mla_get_decode_metadata", lib.mla_get_decode_metadata(
+        ctypes.byref(problem), _ptr(cache_seqlens), ctypes.byref(meta), _stream(stream)))
+    return meta
+
+
+def decode_fwd(problem, q, kv_cache, block_table, cache_seqlens, meta, workspace, out, lse, stream=None):
+    """a2-a9 dense decode (mla_decode_fwd)."""
+    lib = _lib.load()
+    _need(q, "q", torch.bfloat16)
+    _need(kv_cache, "kv_cache", None)
+    _need(block_table, "block_table", torch.int32)
+    _need(cache_seqlens, "cache_seqlens", torch.int32)
+    _need(workspace, "workspace", None)
+    _need(out, "out", None)
+    _need(lse, "lse", torch.float32)
+    _lib.check("mla_decode_fwd", lib.mla_decode_fwd(
+        ctypes.byref(problem), _ptr(q), _ptr(kv_cache), _ptr(block_table), _ptr(cache_seqlens),
+        ctypes.byref(meta), _ptr(workspace), workspace.numel() * workspace.element_size(), _ptr(out), _ptr(lse),
+        _stream(stream)))
+
+
+def sparse_decode_fwd(problem, q, kv_cache, indices, meta, workspace, out, lse, stream=None):
+    """a2-a9 top-k sparse decode (mla_sparse_decode_fwd)."""
+    lib = _lib.load()
+    _need(q, "q", torch.bfloat16)
+    _need(kv_cache, "kv_cache", None)
+    _need(indices, "indices", torch.int32)
+    _need(workspace, "workspace", None)
+    _need(out, "out", None)
+    _need(lse, "lse", torch.float32)
+    _lib.check("mla_sparse_decode_fwd", lib.mla_sparse_decode_fwd(
+        ctypes.byref(problem), _ptr(q), _ptr(kv_cache), _ptr(indices), ctypes.byref(meta), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _ptr(out), _ptr(lse), _stream(stream)))
+
+
+def combine(num_items, h_q, s_q, o_part, lse_part, split_offsets, out, lse, stream=None):
+    """a9 standalone LSE merge (mla_combine)."""
+    lib = _lib.load()
+    _need(o_part, "o_part", torch.float32)
+    _need(lse_part, "lse_part", torch.float32)
+    _need(split_offsets, "split_offsets", torch.int32)
+    _need(out, "out", None)
+    _need(lse, "lse", torch.float32)
+    od = {torch.bfloat16: _lib.OUT_BF16, torch.float32: _lib.OUT_FP32}[out.dtype]
+    _lib.check("mla_combine", lib.mla_combine(int(num_items), int(h_q), int(s_q), _ptr(o_part), _ptr(lse_part),
+                                              _ptr(split_offsets), od, _ptr(out), _ptr(lse), _stream(stream)))
+
+
+def debug_gather_rows(problem, table_or_indices, cache_seqlens, rows_out, stream=None):
+    lib = _lib.load()
+    _need(table_or_indices, "table_or_indices", torch.int32)
+    _need(rows_out, "rows_out", torch.int32)
+    _lib.check("mla_debug_gather_rows", lib.mla_debug_gather_rows(
+        ctypes.byref(problem), _ptr(table_or_indices), _ptr(cache_seqlens), _ptr(rows_out), _stream(stream)))
+
+
+class Decoder:
+    """Owns the per-shape plan, metadata buffer, workspace and outputs for one
+    decode problem; ``step()`` runs the whole hot path (metadata + decode)."""
+
+    def __init__(self, problem, device="cuda", num_cus=0):
+        self.problem = problem
+        self.meta = plan(problem, num_cus)
+        dev = torch.device(device)
+        self.meta_buf = torch.zeros((self.meta.bytes + 15) // 16 * 4, dtype=torch.int32, device=dev)
+        self.workspace = torch.empty(max(16, (workspace_bytes(self.meta) + 15) // 16 * 4), dtype=torch.float32,
+                                     device=dev)
+        B, S, H = problem.batch, problem.s_q, problem.h_q
+        odt = torch.float32 if problem.out_dtype == _lib.OUT_FP32 else torch.bfloat16
+        self.out = torch.empty((B, S, H, 512), dtype=odt, device=dev)
+        self.lse = torch.empty((B, H, S), dtype=torch.float32, device=dev)
+
+    def metadata(self, cache_seqlens=None, stream=None):
+        get_decode_metadata(self.problem, cache_seqlens, self.meta, self.meta_buf, stream)
+
+    def decode(self, q, kv_cache, block_table=None, cache_seqlens=None, indices=None, stream=None):
+        if self.problem.topk > 0:
+            sparse_decode_fwd(self.problem, q, kv_cache, indices, self.meta, self.workspace, self.out, self.lse,
+                              stream)
+        else:
+            decode_fwd(self.problem, q, kv_cache, block_table, cache_seqlens, self.meta, self.workspace, self.out,
+                       self.lse, stream)
+        return self.out, self.lse
+
+    def step(self, q, kv_cache, block_table=None, cache_seqlens=None, indices=None, stream=None):
+        self.metadata(cache_seqlens, stream)
+        return self.decode(q, kv_cache, block_table, cache_seqlens, indices, stream)
+
+    @classmethod
+    def for_workload(cls, w, device="cuda", num_cus=0):
+        p = make_problem(w.batch, w.s_q, w.h_q, w.num_blocks, w.max_blocks_per_seq, topk=w.topk, causal=w.causal,
+                         kv_format=w.kv_format, out_dtype=w.out_dtype, softmax_scale=w.softmax_scale)
+        return cls(p, device, num_cus)
+
+    def run_workload(self, w, stream=None):
+        return self.step(w.q, w.kv, w.block_table, w.cache_seqlens, w.indices, stream)

@@ -1,0 +1,263 @@
+// Host side of the C ABI: validation, planning and launches.
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <mutex>
+
+#include "../../include/mla_decode.h"
+#include "common.h"
+#include "kernels.h"
+
+namespace {
+
+using mla::kBlock;
+
+constexpr int kFixedOverhead = 1;
+constexpr int kMaxDevices = 64;
+
+int g_cu_count[kMaxDevices];
+std::mutex g_cu_mu;
+
+mla_status_t device_cus(int32_t* out) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return MLA_ERR_HIP;
+    std::lock_guard<std::mutex> g(g_cu_mu);
+    if (g_cu_count[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+            return MLA_ERR_HIP;
+        g_cu_count[dev] = n;
+    }
+    *out = g_cu_count[dev];
+    return MLA_OK;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+mla_status_t validate(const mla_problem_t* p) {
+    if (!p) return MLA_ERR_INVALID_ARG;
+    if (p->batch < 1 || p->s_q < 1 || p->h_q < 1 || p->num_blocks < 1) return MLA_ERR_INVALID_ARG;
+    if (p->topk < 0 || p->max_blocks_per_seq < 0) return MLA_ERR_INVALID_ARG;
+    if (p->causal != 0 && p->causal != 1) return MLA_ERR_INVALID_ARG;
+    if (p->kv_format != MLA_KV_BF16_576 && p->kv_format != MLA_KV_FP8_656) return MLA_ERR_INVALID_ARG;
+    if (p->out_dtype != MLA_OUT_BF16 && p->out_dtype != MLA_OUT_FP32) return MLA_ERR_INVALID_ARG;
+    if (!std::isfinite(p->softmax_scale)) return MLA_ERR_INVALID_ARG;
+    if (p->h_kv != 1 || p->d_qk != mla::kDqk || p->d_v != mla::kDv || p->block_size != kBlock)
+        return MLA_ERR_UNSUPPORTED;
+    if (p->topk == 0 && p->max_blocks_per_seq < 1) return MLA_ERR_INVALID_ARG;
+    if (p->topk > 0 && p->causal) return MLA_ERR_UNSUPPORTED;
+    const int64_t items = (int64_t)p->batch * p->s_q;
+    if (items > mla::kMaxMetaItems) return MLA_ERR_UNSUPPORTED;
+    const int64_t tiles = p->topk > 0 ? ((int64_t)p->topk + 63) / 64 : (int64_t)p->max_blocks_per_seq;
+    if (items * (tiles + kFixedOverhead) >= ((int64_t)1 << 31)) return MLA_ERR_UNSUPPORTED;
+    if ((int64_t)p->num_blocks * kBlock >= ((int64_t)1 << 31)) return MLA_ERR_UNSUPPORTED;
+    // the sparse bf16 gather addresses rows with 32-bit buffer offsets
+    if (p->topk > 0 && p->kv_format == MLA_KV_BF16_576 &&
+        (int64_t)p->num_blocks * kBlock * mla::kRowBytes >= ((int64_t)1 << 32))
+        return MLA_ERR_UNSUPPORTED;
+    if ((int64_t)items * p->h_q * mla::kDv >= ((int64_t)1 << 40)) return MLA_ERR_UNSUPPORTED;
+    return MLA_OK;
+}
+
+bool same_problem(const mla_problem_t& a, const mla_problem_t& b) {
+    return a.batch == b.batch && a.s_q == b.s_q && a.h_q == b.h_q && a.h_kv == b.h_kv && a.d_qk == b.d_qk &&
+           a.d_v == b.d_v && a.block_size == b.block_size && a.num_blocks == b.num_blocks &&
+           a.max_blocks_per_seq == b.max_blocks_per_seq && a.topk == b.topk && a.causal == b.causal &&
+           a.kv_format == b.kv_format && a.out_dtype == b.out_dtype && a.softmax_scale == b.softmax_scale;
+}
+
+size_t meta_bytes(int64_t parts, int64_t items) {
+    return (size_t)(mla::kMetaHeader + mla::kMetaRec * parts + items + 1) * sizeof(int32_t);
+}
+
+mla_status_t check_meta(const mla_problem_t* p, const mla_metadata_t* m) {
+    if (!m || !m->dev || !aligned16(m->dev)) return MLA_ERR_INVALID_ARG;
+    if (!same_problem(m->sig, *p)) return MLA_ERR_METADATA_MISMATCH;
+    const int64_t items = (int64_t)p->batch * p->s_q;
+    if (m->num_partitions < 1 || m->num_head_blocks != (p->h_q + 63) / 64 ||
+        m->fixed_overhead != kFixedOverhead || m->max_splits != items + m->num_partitions ||
+        m->bytes < meta_bytes(m->num_partitions, items))
+        return MLA_ERR_METADATA_MISMATCH;
+    return MLA_OK;
+}
+
+mla_status_t run_decode(const mla_problem_t* p, bool sparse, const void* q, const void* kv,
+                        const int32_t* block_table, const int32_t* cache_seqlens, const int32_t* indices,
+                        const mla_metadata_t* meta, void* ws, size_t ws_bytes, void* out, float* lse,
+                        void* stream) {
+    mla_status_t st = validate(p);
+    if (st != MLA_OK) return st;
+    if (sparse != (p->topk > 0)) return MLA_ERR_INVALID_ARG;
+    if (!q || !kv || !out || !lse || !aligned16(q) || !aligned16(kv) || !aligned16(out))
+        return MLA_ERR_INVALID_ARG;
+    if (sparse ? !indices : (!block_table || !cache_seqlens)) return MLA_ERR_INVALID_ARG;
+    st = check_meta(p, meta);
+    if (st != MLA_OK) return st;
+    const size_t need = mla_workspace_bytes(meta);
+    if (!ws || !aligned16(ws)) return need == 0 ? MLA_ERR_INVALID_ARG : MLA_ERR_WORKSPACE_TOO_SMALL;
+    if (ws_bytes < need) return MLA_ERR_WORKSPACE_TOO_SMALL;
+
+    const int64_t slots = meta->max_splits;
+    mla::DecodeArgs a{};
+    a.q = q;
+    a.kv = kv;
+    a.block_table = block_table;
+    a.cache_seqlens = cache_seqlens;
+    a.indices = indices;
+    a.meta = (const int32_t*)meta->dev;
+    a.o_part = (float*)ws;
+    a.lse_part = (float*)ws + slots * p->h_q * mla::kDv;
+    a.out = out;
+    a.lse = lse;
+    a.num_rows = (int64_t)p->num_blocks * kBlock;
+    a.batch = p->batch;
+    a.s_q = p->s_q;
+    a.h_q = p->h_q;
+    a.max_blocks = p->max_blocks_per_seq;
+    a.topk = p->topk;
+    a.causal = p->causal;
+    a.out_fp32 = p->out_dtype == MLA_OUT_FP32;
+    a.num_parts = meta->num_partitions;
+    a.n_hblk = meta->num_head_blocks;
+    a.max_slots = (int)slots;
+    a.scale_log2 = p->softmax_scale * 1.4426950408889634f;
+    hipStream_t s = (hipStream_t)stream;
+    if (mla::launch_decode(a, sparse, p->kv_format == MLA_KV_FP8_656, s) != hipSuccess) return MLA_ERR_HIP;
+
+    mla::CombineArgs c{};
+    c.o_part = a.o_part;
+    c.lse_part = a.lse_part;
+    c.split_offsets = a.meta + mla::kMetaHeader + mla::kMetaRec * meta->num_partitions;
+    c.out = out;
+    c.lse = lse;
+    c.num_items = p->batch * p->s_q;
+    c.h_q = p->h_q;
+    c.s_q = p->s_q;
+    c.out_fp32 = a.out_fp32;
+    c.skip_single = 1;
+    if (mla::launch_combine(c, s) != hipSuccess) return MLA_ERR_HIP;
+    return MLA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t mla_abi_version(void) { return MLA_DECODE_ABI_VERSION; }
+
+const char* mla_status_string(mla_status_t s) {
+    switch (s) {
+        case MLA_OK: return "ok";
+        case MLA_ERR_INVALID_ARG: return "invalid argument";
+        case MLA_ERR_UNSUPPORTED: return "unsupported problem";
+        case MLA_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
+        case MLA_ERR_METADATA_MISMATCH: return "metadata was planned for another problem";
+        case MLA_ERR_HIP: return "HIP runtime error";
+    }
+    return "unknown status";
+}
+
+mla_status_t mla_plan(const mla_problem_t* problem, int32_t num_cus, mla_metadata_t* meta) {
+    if (!meta || num_cus < 0) return MLA_ERR_INVALID_ARG;
+    mla_status_t st = validate(problem);
+    if (st != MLA_OK) return st;
+    if (num_cus == 0) {
+        st = device_cus(&num_cus);
+        if (st != MLA_OK) return st;
+    }
+    const int32_t hblk = (problem->h_q + 63) / 64;
+    int32_t parts = num_cus / hblk;
+    if (parts < 1) parts = 1;
+    const int64_t items = (int64_t)problem->batch * problem->s_q;
+    meta->sig = *problem;
+    meta->num_partitions = parts;
+    meta->num_head_blocks = hblk;
+    meta->fixed_overhead = kFixedOverhead;
+    meta->max_splits = (int32_t)(items + parts);
+    meta->dev = nullptr;
+    meta->bytes = meta_bytes(parts, items);
+    return MLA_OK;
+}
+
+size_t mla_workspace_bytes(const mla_metadata_t* meta) {
+    if (!meta) return 0;
+    return (size_t)meta->max_splits * (size_t)meta->sig.h_q * (mla::kDv + 1) * sizeof(float);
+}
+
+mla_status_t mla_get_decode_metadata(const mla_problem_t* problem, const int32_t* cache_seqlens,
+                                     mla_metadata_t* meta, void* stream) {
+    mla_status_t st = validate(problem);
+    if (st != MLA_OK) return st;
+    st = check_meta(problem, meta);
+    if (st != MLA_OK) return st;
+    if (problem->topk == 0 && !cache_seqlens) return MLA_ERR_INVALID_ARG;
+    mla::MetaArgs a{};
+    a.cache_seqlens = cache_seqlens;
+    a.meta = (int32_t*)meta->dev;
+    a.batch = problem->batch;
+    a.s_q = problem->s_q;
+    a.max_blocks = problem->max_blocks_per_seq;
+    a.topk = problem->topk;
+    a.causal = problem->causal;
+    a.num_parts = meta->num_partitions;
+    a.fixed_overhead = meta->fixed_overhead;
+    return mla::launch_metadata(a, (hipStream_t)stream) == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+}
+
+mla_status_t mla_decode_fwd(const mla_problem_t* problem, const void* q, const void* kv_cache,
+                            const int32_t* block_table, const int32_t* cache_seqlens, const mla_metadata_t* meta,
+                            void* workspace, size_t workspace_bytes, void* out, float* lse, void* stream) {
+    return run_decode(problem, false, q, kv_cache, block_table, cache_seqlens, nullptr, meta, workspace,
+                      workspace_bytes, out, lse, stream);
+}
+
+mla_status_t mla_sparse_decode_fwd(const mla_problem_t* problem, const void* q, const void* kv_cache,
+                                   const int32_t* indices, const mla_metadata_t* meta, void* workspace,
+                                   size_t workspace_bytes, void* out, float* lse, void* stream) {
+    return run_decode(problem, true, q, kv_cache, nullptr, nullptr, indices, meta, workspace, workspace_bytes,
+                      out, lse, stream);
+}
+
+mla_status_t mla_combine(int32_t num_items, int32_t h_q, int32_t s_q, const float* o_part, const float* lse_part,
+                         const int32_t* split_offsets, int32_t out_dtype, void* out, float* lse, void* stream) {
+    if (num_items < 1 || h_q < 1 || s_q < 1 || num_items % s_q != 0) return MLA_ERR_INVALID_ARG;
+    if (!o_part || !lse_part || !split_offsets || !out || !lse) return MLA_ERR_INVALID_ARG;
+    if (!aligned16(o_part) || !aligned16(out)) return MLA_ERR_INVALID_ARG;
+    if (out_dtype != MLA_OUT_BF16 && out_dtype != MLA_OUT_FP32) return MLA_ERR_INVALID_ARG;
+    if ((int64_t)num_items * h_q >= ((int64_t)1 << 31) / 4) return MLA_ERR_UNSUPPORTED;
+    mla::CombineArgs c{};
+    c.o_part = o_part;
+    c.lse_part = lse_part;
+    c.split_offsets = split_offsets;
+    c.out = out;
+    c.lse = lse;
+    c.num_items = num_items;
+    c.h_q = h_q;
+    c.s_q = s_q;
+    c.out_fp32 = out_dtype == MLA_OUT_FP32;
+    c.skip_single = 0;
+    return mla::launch_combine(c, (hipStream_t)stream) == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+}
+
+mla_status_t mla_debug_gather_rows(const mla_problem_t* problem, const int32_t* table_or_indices,
+                                   const int32_t* cache_seqlens, int32_t* rows_out, void* stream) {
+    mla_status_t st = validate(problem);
+    if (st != MLA_OK) return st;
+    if (!table_or_indices || !rows_out || (problem->topk == 0 && !cache_seqlens)) return MLA_ERR_INVALID_ARG;
+    mla::GatherArgs g{};
+    g.table_or_indices = table_or_indices;
+    g.cache_seqlens = cache_seqlens;
+    g.rows_out = rows_out;
+    g.num_rows = (int64_t)problem->num_blocks * kBlock;
+    g.batch = problem->batch;
+    g.s_q = problem->s_q;
+    g.max_blocks = problem->max_blocks_per_seq;
+    g.topk = problem->topk;
+    g.causal = problem->causal;
+    g.row_stride = problem->topk > 0 ? 64 * ((problem->topk + 63) / 64) : 64 * problem->max_blocks_per_seq;
+    return mla::launch_gather(g, (hipStream_t)stream) == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+}
+
+}  // extern "C"

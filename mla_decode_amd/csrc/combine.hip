@@ -1,0 +1,82 @@
+// a9: LSE merge of split partials, plus the a2 debug gather.
+//
+// Combine: one workgroup per (item, 4 heads); 64 lanes x 8 dims cover the 512
+// output dims of a head.  With m* = max_k lse_k and w_k = exp(lse_k - m*):
+// out = sum_k w_k o_k / sum_k w_k and lse = m* + ln sum_k w_k, which is the
+// pairwise split merge applied to all partials at once.
+
+#include "common.h"
+#include "kernels.h"
+
+namespace mla {
+
+__global__ void __launch_bounds__(256) combine_kernel(const CombineArgs a) {
+    const int item = blockIdx.x;
+    const int h = blockIdx.y * 4 + (threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    if (h >= a.h_q) return;
+    const int s0 = a.split_offsets[item], s1 = a.split_offsets[item + 1];
+    const int n = s1 - s0;
+    if (a.skip_single && n == 1) return;
+    const int H = a.h_q;
+    float m = -INFINITY;
+    for (int k = s0; k < s1; ++k) m = fmaxf(m, a.lse_part[(int64_t)k * H + h]);
+    float o[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    float lse_v = -INFINITY;
+    if (n > 0 && m != -INFINITY) {
+        float wsum = 0.f;
+        for (int k = s0; k < s1; ++k) {
+            const float lk = a.lse_part[(int64_t)k * H + h];
+            const float w = lk == -INFINITY ? 0.f : __expf(lk - m);
+            wsum += w;
+            const f32x4* src = (const f32x4*)(a.o_part + ((int64_t)k * H + h) * kDv + lane * 8);
+            const f32x4 u = src[0], v = src[1];
+            o[0] += w * u[0]; o[1] += w * u[1]; o[2] += w * u[2]; o[3] += w * u[3];
+            o[4] += w * v[0]; o[5] += w * v[1]; o[6] += w * v[2]; o[7] += w * v[3];
+        }
+        const float inv = 1.f / wsum;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o[e] *= inv;
+        lse_v = m + __logf(wsum);
+    }
+    const int64_t off = ((int64_t)item * H + h) * kDv + lane * 8;
+    if (a.out_fp32) {
+        f32x4* dst = (f32x4*)((float*)a.out + off);
+        dst[0] = f32x4{o[0], o[1], o[2], o[3]};
+        dst[1] = f32x4{o[4], o[5], o[6], o[7]};
+    } else {
+        bf16x8 w;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) w[e] = (__bf16)o[e];
+        *(bf16x8*)((__bf16*)a.out + off) = w;
+    }
+    if (lane == 0) {
+        const int b = item / a.s_q, i = item - b * a.s_q;
+        a.lse[((int64_t)b * H + h) * a.s_q + i] = lse_v;
+    }
+}
+
+hipError_t launch_combine(const CombineArgs& a, hipStream_t stream) {
+    const dim3 grid(a.num_items, (a.h_q + 3) / 4), block(256);
+    hipLaunchKernelGGL(combine_kernel, grid, block, 0, stream, a);
+    return hipGetLastError();
+}
+
+// a2 test hook: the rows the decode kernels read, through the same resolver.
+__global__ void __launch_bounds__(256) gather_kernel(const GatherArgs a) {
+    const int j = blockIdx.x;
+    const bool sparse = a.topk > 0;
+    RowResolver rr{sparse ? nullptr : a.table_or_indices, a.cache_seqlens, sparse ? a.table_or_indices : nullptr,
+                   a.s_q, a.max_blocks, a.topk, a.causal, a.num_rows};
+    const int nslots = rr.slots(j);
+    const int ntiles = (nslots + 63) >> 6;
+    for (int t = threadIdx.x; t < ntiles * 64 && t < a.row_stride; t += blockDim.x)
+        a.rows_out[(int64_t)j * a.row_stride + t] = (int32_t)rr.row(j, t, nslots);
+}
+
+hipError_t launch_gather(const GatherArgs& a, hipStream_t stream) {
+    hipLaunchKernelGGL(gather_kernel, dim3(a.batch * a.s_q), dim3(256), 0, stream, a);
+    return hipGetLastError();
+}
+
+}  // namespace mla

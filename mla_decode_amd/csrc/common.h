@@ -1,0 +1,107 @@
+// Device-side building blocks shared by the gfx950 decode kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mla {
+
+constexpr int kDqk = 576;          // latent 512 + RoPE 64
+constexpr int kDv = 512;
+constexpr int kBlock = 64;         // cache page = KV tile, in tokens
+constexpr int kHeadsPerWG = 64;    // query heads per workgroup
+constexpr int kWaves = 4;
+constexpr int kThreads = kWaves * 64;
+constexpr int kRowBytes = kDqk * 2;          // 1152
+constexpr int kRowChunks = kRowBytes / 16;   // 72 chunks of 16 B
+constexpr int kTileBytes = kBlock * kRowBytes;  // 73728
+constexpr int kFp8RowBytes = 656;
+constexpr int kMetaHeader = 8;
+constexpr int kMetaRec = 5;
+constexpr int32_t kMetaMagic = 0x4D4C4131;
+
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4;
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
+typedef __attribute__((__vector_size__(4 * sizeof(int)))) int i32x4;
+typedef __attribute__((__vector_size__(2 * sizeof(int)))) int i32x2;
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef const __attribute__((address_space(1))) void gbl_void_t;
+
+// LDS tile layout: token t's 16-byte chunk c (c in [0, 72)) lives at chunk
+// index t*72 + (c ^ swz(t)).  The XOR only touches the low three bits, so a
+// chunk stays inside its aligned group of eight.  swz(t) is a bijection over
+// each run of 8 tokens of equal parity and maps tokens 4v+k and 4v+k+2 to
+// values that differ above bit 0; with a row pitch of 72 chunks this makes
+//  - 16 consecutive tokens reading the same chunk (the K operand) hit 16
+//    distinct 16-byte bank groups of a 256-byte bank window, and
+//  - 4 consecutive tokens reading a 2-chunk column pair (the transposed V
+//    operand read) hit 8 distinct bank groups.
+__device__ __forceinline__ int swz(int t) {
+    int u = (t >> 1) & 7;
+    return ((u & 1) << 2) | (u >> 1);
+}
+__device__ __forceinline__ int lds_chunk(int t, int c) { return t * kRowChunks + (c ^ swz(t)); }
+
+__device__ __forceinline__ int visible_len(int L, int s_q, int i, int causal) {
+    if (!causal) return L;
+    int v = L - s_q + 1 + i;
+    return v < 0 ? 0 : (v > L ? L : v);
+}
+
+// Clamp a cache length read from device memory to what the block table holds.
+__device__ __forceinline__ int clamp_len(int L, int max_blocks) {
+    int cap = max_blocks * kBlock;
+    return L < 0 ? 0 : (L > cap ? cap : L);
+}
+
+// a2: physical cache row of a KV slot, or -1 if the slot is masked.
+// Dense: slot = logical token of request b, read through its page table; a
+// page id outside [0, num_blocks) masks its whole page.  Sparse: slot = top-k
+// entry holding page*64 + offset; entries < 0 or >= num_rows are masked.
+__device__ __forceinline__ bool page_ok(int page, int64_t num_rows) {
+    return page >= 0 && (int64_t)page * kBlock < num_rows;
+}
+__device__ __forceinline__ int64_t row_in_page(int page, int tok, int tok_valid, int64_t num_rows) {
+    return (tok < tok_valid && page_ok(page, num_rows)) ? (int64_t)page * kBlock + tok : -1;
+}
+__device__ __forceinline__ int64_t sparse_entry_row(int64_t r, int64_t num_rows) {
+    return (r < 0 || r >= num_rows) ? -1 : r;
+}
+
+struct RowResolver {
+    const int32_t* block_table;    // dense
+    const int32_t* cache_seqlens;  // dense
+    const int32_t* indices;        // sparse
+    int s_q, max_blocks, topk, causal;
+    int64_t num_rows;
+
+    // number of KV slots of item j (dense: causal-visible tokens; sparse: topk)
+    __device__ __forceinline__ int slots(int j) const {
+        if (topk > 0) return topk;
+        int b = j / s_q, i = j - b * s_q;
+        return visible_len(clamp_len(cache_seqlens[b], max_blocks), s_q, i, causal);
+    }
+    __device__ __forceinline__ int page(int j, int tile) const {
+        return block_table[(int64_t)(j / s_q) * max_blocks + tile];
+    }
+    __device__ __forceinline__ int64_t row(int j, int slot, int nslots) const {
+        if (slot >= nslots) return -1;
+        if (topk > 0) return sparse_entry_row(indices[(int64_t)j * topk + slot], num_rows);
+        return row_in_page(page(j, slot >> 6), slot & 63, nslots - (slot & ~63), num_rows);
+    }
+};
+
+__device__ __forceinline__ float wave_max_pair(float x) {
+    // lanes l and l^32 hold one head's two halves; after the swap both lanes
+    // see both values
+    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float wave_sum_pair(float x) {
+    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+}  // namespace mla

@@ -1,0 +1,56 @@
+// Launch interfaces between the host API and the gfx950 kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mla {
+
+struct DecodeArgs {
+    const void* q;               // bf16 [B, S, H, 576]
+    const void* kv;              // bf16 rows of 1152 B or fp8 rows of 656 B
+    const int32_t* block_table;  // dense
+    const int32_t* cache_seqlens;
+    const int32_t* indices;      // sparse
+    const int32_t* meta;         // scheduler metadata (device)
+    float* o_part;               // [max_slots, H, 512]
+    float* lse_part;             // [max_slots, H]
+    void* out;                   // [B, S, H, 512]
+    float* lse;                  // [B, H, S]
+    int64_t num_rows;            // num_blocks * 64
+    int batch, s_q, h_q, max_blocks, topk, causal, out_fp32;
+    int num_parts, n_hblk, max_slots;
+    float scale_log2;            // softmax_scale * log2(e)
+};
+
+struct MetaArgs {
+    const int32_t* cache_seqlens;
+    int32_t* meta;
+    int batch, s_q, max_blocks, topk, causal, num_parts, fixed_overhead;
+};
+
+struct CombineArgs {
+    const float* o_part;
+    const float* lse_part;
+    const int32_t* split_offsets;
+    void* out;
+    float* lse;
+    int num_items, h_q, s_q, out_fp32, skip_single;
+};
+
+struct GatherArgs {
+    const int32_t* table_or_indices;
+    const int32_t* cache_seqlens;
+    int32_t* rows_out;
+    int64_t num_rows;
+    int batch, s_q, max_blocks, topk, causal, row_stride;
+};
+
+hipError_t launch_decode(const DecodeArgs& a, bool sparse, bool fp8, hipStream_t stream);
+hipError_t launch_metadata(const MetaArgs& a, hipStream_t stream);
+hipError_t launch_combine(const CombineArgs& a, hipStream_t stream);
+hipError_t launch_gather(const GatherArgs& a, hipStream_t stream);
+
+constexpr int kMaxMetaItems = 16384;   // batch * s_q handled by the one-workgroup scheduler
+
+}  // namespace mla

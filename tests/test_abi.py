@@ -1,0 +1,110 @@
+"""The C-ABI library loads, exports every declared entry point, and validates
+arguments on the host (no GPU needed: mla_plan with an explicit CU count and
+the argument checks that fail before any launch)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from conftest import ROOT
+
+
+def _declared():
+    names = []
+    for f in os.listdir(os.path.join(ROOT, "include")):
+        if f.endswith(".h"):
+            src = open(os.path.join(ROOT, "include", f)).read()
+            names += re.findall(r"^\s*(?:[\w\s\*]+?)\b(mla_\w+)\s*\(", src, flags=re.M)
+    return sorted(set(names))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from mla_decode_amd import _lib
+    return _lib.load()
+
+
+def test_exports_every_declared_symbol(lib):
+    from mla_decode_amd import _lib
+    names = _declared()
+    assert set(names) == set(_lib.EXPORTED), names
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_abi_version_and_status_strings(lib):
+    assert lib.mla_abi_version() == 1
+    for s in range(6):
+        assert lib.mla_status_string(s)
+    assert lib.mla_status_string(99) == b"unknown status"
+
+
+def _problem(**kw):
+    import mla_decode_amd as mla
+    base = dict(batch=64, s_q=1, h_q=128, num_blocks=4096, max_blocks_per_seq=64)
+    base.update(kw)
+    args = {k: base.pop(k) for k in ("batch", "s_q", "h_q", "num_blocks", "max_blocks_per_seq")}
+    return mla.make_problem(**args, **base)
+
+
+def test_plan_host_only():
+    import mla_decode_amd as mla
+    m = mla.plan(_problem(), num_cus=256)
+    assert m.num_head_blocks == 2 and m.num_partitions == 128 and m.fixed_overhead == 1
+    assert m.max_splits == 64 + 128
+    assert m.bytes == (8 + 5 * 128 + 64 + 1) * 4
+    assert mla.workspace_bytes(m) == 192 * 128 * 513 * 4
+    m = mla.plan(_problem(h_q=16, batch=2, num_blocks=8, max_blocks_per_seq=4), num_cus=256)
+    assert m.num_head_blocks == 1 and m.num_partitions == 256
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(batch=0), 1), (dict(s_q=0), 1), (dict(h_q=0), 1), (dict(num_blocks=0), 1),
+    (dict(max_blocks_per_seq=0), 1), (dict(topk=-1), 1), (dict(softmax_scale=float("nan")), 1),
+    (dict(topk=64, causal=True), 2), (dict(batch=20000), 2),
+])
+def test_plan_rejects(kw, status):
+    import mla_decode_amd as mla
+    with pytest.raises(mla.MlaError) as e:
+        mla.plan(_problem(**kw), num_cus=256)
+    assert e.value.status == status
+
+
+def test_unsupported_shapes(lib):
+    import mla_decode_amd as mla
+    for field, val in (("h_kv", 2), ("d_qk", 512), ("d_v", 256), ("block_size", 32)):
+        p = _problem()
+        setattr(p, field, val)
+        m = mla.Metadata()
+        assert lib.mla_plan(ctypes.byref(p), 256, ctypes.byref(m)) == 2
+
+
+def test_decode_rejects_bad_arguments_before_launch(lib):
+    import mla_decode_amd as mla
+    p = _problem()
+    m = mla.plan(p, num_cus=256)
+    ws = mla.workspace_bytes(m)
+    fake = ctypes.c_void_p(1 << 20)       # never dereferenced: validation fails first
+    # metadata has no device buffer
+    assert lib.mla_decode_fwd(ctypes.byref(p), fake, fake, fake, fake, ctypes.byref(m), fake, ws, fake, fake,
+                              None) == 1
+    m.dev = 1 << 20
+    # workspace too small
+    assert lib.mla_decode_fwd(ctypes.byref(p), fake, fake, fake, fake, ctypes.byref(m), fake, ws - 1, fake, fake,
+                              None) == 3
+    # misaligned q
+    assert lib.mla_decode_fwd(ctypes.byref(p), ctypes.c_void_p((1 << 20) + 2), fake, fake, fake,
+                              ctypes.byref(m), fake, ws, fake, fake, None) == 1
+    # metadata planned for another problem
+    p2 = _problem(batch=32)
+    assert lib.mla_decode_fwd(ctypes.byref(p2), fake, fake, fake, fake, ctypes.byref(m), fake, ws, fake, fake,
+                              None) == 4
+    # sparse entry point on a dense problem
+    assert lib.mla_sparse_decode_fwd(ctypes.byref(p), fake, fake, fake, ctypes.byref(m), fake, ws, fake, fake,
+                                     None) == 1
+    # combine argument checks
+    assert lib.mla_combine(0, 128, 1, fake, fake, fake, 0, fake, fake, None) == 1
+    assert lib.mla_combine(3, 128, 2, fake, fake, fake, 0, fake, fake, None) == 1
+    assert lib.mla_combine(4, 128, 2, fake, fake, fake, 7, fake, fake, None) == 1
