@@ -1,0 +1,185 @@
+"""Benchmark: absorbed-MLA decode on one MI355X.
+
+A step is one pass of the whole hot path over one batch: the split-KV
+scheduler (mla_get_decode_metadata) followed by the decode call
+(mla_decode_fwd: partial-attention kernel + LSE combine), on the DeepSeek-V3
+decode shape b=64, s_q=1, h_q=128, seqlen=4096 (64-token pages shuffled over
+a 4096-page pool, bf16 N(0,1) inputs, inputs resident in HBM).
+
+Prints one JSON line.  ``value`` is TFLOP/s of algorithmic work (FLOPs =
+2 h_q (576 + 512) per visible query-token/KV-token pair) per step; the line
+also carries HBM GB/s and microseconds per step, the roofline of the decode
+call (HBM-bound at this shape), and the fp64 CPU oracle timed on the host.
+"""
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+MFMA_BF16_PEAK_TFLOPS = 2516.6  # MI355X dense bf16 MFMA, published (256 CU x 2.4 GHz x 4096)
+METRIC = "MLA decode TFLOPS + HBM GB/s, µs/step at b=64,h_q=128,seqlen=4096 (1 GPU)"
+KERNEL_SOURCES = ("mla_decode_amd/csrc/decode.hip", "mla_decode_amd/csrc/common.h")
+COUNTERS_FILE = os.path.join(ROOT, "profiles", "decode_kernel_config2_counters.json")
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic():
+    """HBM bytes per decode launch from the committed rocprofv3 counter runs,
+    or None when they are missing or were taken on other kernel source."""
+    try:
+        with open(COUNTERS_FILE) as f:
+            c = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if c.get("kernel_source_sha") != kernel_source_hash():
+        return None
+    return c.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(w, flops):
+    """The fp64 oracle on the same workload, on this host's cores."""
+    import numpy as np
+    import threadpoolctl
+    import torch
+    from oracle import attention as A
+    q = w.q.cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
+    kv = w.kv.cpu().contiguous().view(torch.int16).numpy().view(np.uint16).reshape(-1, 576)
+    bt = w.block_table.cpu().numpy()
+    sl = w.cache_seqlens.cpu().numpy()
+    threads = max(i.get("num_threads", 1) for i in threadpoolctl.threadpool_info() if i.get("user_api") == "blas")
+    t0 = time.perf_counter()
+    A.decode(q, kv, w.softmax_scale, block_table=bt, cache_seqlens=sl, causal=w.causal)
+    dt = time.perf_counter() - t0
+    return {"value": flops / dt / 1e12, "unit": "TFLOPS", "cores": int(threads), "kind": "oracle",
+            "sample": f"one full step (all {w.batch} requests x {w.h_q} heads x 4096 tokens), fp64 numpy, "
+                      f"{dt:.2f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a 1 GiB device copy 5 times (reference for HBM byte counters)")
+    args = ap.parse_args()
+    if args.calibrate_copy:
+        import torch
+        n = 1 << 30
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_per_launch": n, "launches": 5}), flush=True)
+        return
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (the decode path has no multi-GPU code); got --gpus {args.gpus}",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import mla_decode_amd as mla
+    from workloads import make_config, flops_and_bytes
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    w = make_config(2, device=dev)
+    acct = flops_and_bytes(w)
+    dec = mla.Decoder.for_workload(w, dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step():
+        dec.metadata(w.cache_seqlens, stream)
+        dec.decode(w.q, w.kv, w.block_table, w.cache_seqlens, None, stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # timed region: exactly K whole steps
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(args.steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms_step = e0.elapsed_time(e1) / args.steps
+
+    # decode call alone (partial-attention kernel + combine), same stream, same inputs
+    k0 = torch.cuda.Event(enable_timing=True)
+    k1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    k0.record(stream)
+    for _ in range(args.steps):
+        dec.decode(w.q, w.kv, w.block_table, w.cache_seqlens, None, stream)
+    k1.record(stream)
+    torch.cuda.synchronize()
+    ms_decode = k0.elapsed_time(k1) / args.steps
+
+    # scheduler alone
+    m0 = torch.cuda.Event(enable_timing=True)
+    m1 = torch.cuda.Event(enable_timing=True)
+    m0.record(stream)
+    for _ in range(args.steps):
+        dec.metadata(w.cache_seqlens, stream)
+    m1.record(stream)
+    torch.cuda.synchronize()
+    ms_meta = m0.elapsed_time(m1) / args.steps
+
+    flops, nbytes = acct["flops"], acct["bytes"]
+    tflops = flops / (ms_step * 1e-3) / 1e12
+    gbs = nbytes / (ms_step * 1e-3) / 1e9
+    dec_gbs = nbytes / (ms_decode * 1e-3) / 1e9
+    dec_tflops = flops / (ms_decode * 1e-3) / 1e12
+    line = {
+        "metric": METRIC,
+        "value": round(tflops, 2),
+        "unit": "TFLOPS",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "us_per_step": round(ms_step * 1e3, 2),
+        "hbm_gbs": round(gbs, 1),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "dense absorbed-MLA decode b=64 s_q=1 h_q=128 seqlen=4096 (64-token pages, "
+                               "4096-page shuffled pool, bf16 q/kv N(0,1))",
+                   "batch": w.batch, "s_q": w.s_q, "h_q": w.h_q, "seqlen": 4096, "d_qk": 576, "d_v": 512,
+                   "block_size": 64, "kv_format": "bf16", "step": "metadata + decode (partial + combine)"},
+        "roofline": {"bound": "hbm", "kernel": "mla_decode_fwd (decode_kernel + combine_kernel)",
+                     "achieved": round(dec_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(dec_gbs / HBM_PEAK_GBS, 4), "traffic": measured_traffic(),
+                     "algorithmic_bytes": nbytes, "us_per_launch": round(ms_decode * 1e3, 2)},
+        "roofline_mfma": {"achieved": round(dec_tflops, 1), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                          "frac": round(dec_tflops / MFMA_BF16_PEAK_TFLOPS, 4), "algorithmic_flops": flops},
+        "metadata_us": round(ms_meta * 1e3, 2),
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(w, flops)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()
