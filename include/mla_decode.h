@@ -83,7 +83,7 @@ typedef struct {
     int32_t causal;              /* dense only: bottom-right causal over the s_q tokens */
     int32_t kv_format;           /* mla_kv_format_t */
     int32_t out_dtype;           /* mla_out_dtype_t */
-    float softmax_scale;         /* multiplies q . k before the softmax */
+    float softmax_scale;         /* > 0; multiplies q . k before the softmax */
 } mla_problem_t;
 
 /* Split-KV schedule for one problem shape.  ``mla_plan`` fills everything
@@ -96,7 +96,7 @@ typedef struct {
 typedef struct {
     mla_problem_t sig;           /* problem the plan was made for */
     int32_t num_partitions;      /* P: workgroup columns of the split-KV grid */
-    int32_t num_head_blocks;     /* ceil(h_q / 64) */
+    int32_t num_head_blocks;     /* ceil(h_q / 128) */
     int32_t fixed_overhead;      /* F: per-item cost added by the scheduler */
     int32_t max_splits;          /* upper bound of split slots: batch*s_q + P */
     void *dev;                   /* caller-owned device buffer, >= bytes */

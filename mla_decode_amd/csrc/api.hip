@@ -43,7 +43,7 @@ mla_status_t validate(const mla_problem_t* p) {
     if (p->causal != 0 && p->causal != 1) return MLA_ERR_INVALID_ARG;
     if (p->kv_format != MLA_KV_BF16_576 && p->kv_format != MLA_KV_FP8_656) return MLA_ERR_INVALID_ARG;
     if (p->out_dtype != MLA_OUT_BF16 && p->out_dtype != MLA_OUT_FP32) return MLA_ERR_INVALID_ARG;
-    if (!std::isfinite(p->softmax_scale)) return MLA_ERR_INVALID_ARG;
+    if (!std::isfinite(p->softmax_scale) || !(p->softmax_scale > 0.f)) return MLA_ERR_INVALID_ARG;
     if (p->h_kv != 1 || p->d_qk != mla::kDqk || p->d_v != mla::kDv || p->block_size != kBlock)
         return MLA_ERR_UNSUPPORTED;
     if (p->topk == 0 && p->max_blocks_per_seq < 1) return MLA_ERR_INVALID_ARG;
@@ -76,7 +76,7 @@ mla_status_t check_meta(const mla_problem_t* p, const mla_metadata_t* m) {
     if (!m || !m->dev || !aligned16(m->dev)) return MLA_ERR_INVALID_ARG;
     if (!same_problem(m->sig, *p)) return MLA_ERR_METADATA_MISMATCH;
     const int64_t items = (int64_t)p->batch * p->s_q;
-    if (m->num_partitions < 1 || m->num_head_blocks != (p->h_q + 63) / 64 ||
+    if (m->num_partitions < 1 || m->num_head_blocks != (p->h_q + mla::kHeadsPerWG - 1) / mla::kHeadsPerWG ||
         m->fixed_overhead != kFixedOverhead || m->max_splits != items + m->num_partitions ||
         m->bytes < meta_bytes(m->num_partitions, items))
         return MLA_ERR_METADATA_MISMATCH;
@@ -167,7 +167,7 @@ mla_status_t mla_plan(const mla_problem_t* problem, int32_t num_cus, mla_metadat
         st = device_cus(&num_cus);
         if (st != MLA_OK) return st;
     }
-    const int32_t hblk = (problem->h_q + 63) / 64;
+    const int32_t hblk = (problem->h_q + mla::kHeadsPerWG - 1) / mla::kHeadsPerWG;
     int32_t parts = num_cus / hblk;
     if (parts < 1) parts = 1;
     const int64_t items = (int64_t)problem->batch * problem->s_q;

@@ -9,9 +9,10 @@ namespace mla {
 constexpr int kDqk = 576;          // latent 512 + RoPE 64
 constexpr int kDv = 512;
 constexpr int kBlock = 64;         // cache page = KV tile, in tokens
-constexpr int kHeadsPerWG = 64;    // query heads per workgroup
-constexpr int kWaves = 4;
+constexpr int kHeadsPerWG = 128;   // query heads per workgroup
+constexpr int kWaves = 8;          // two per SIMD
 constexpr int kThreads = kWaves * 64;
+constexpr int kSubTok = 32;        // tokens per compute tile (half a page)
 constexpr int kRowBytes = kDqk * 2;          // 1152
 constexpr int kRowChunks = kRowBytes / 16;   // 72 chunks of 16 B
 constexpr int kTileBytes = kBlock * kRowBytes;  // 73728
@@ -29,20 +30,26 @@ typedef __attribute__((__vector_size__(2 * sizeof(int)))) int i32x2;
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef const __attribute__((address_space(1))) void gbl_void_t;
 
-// LDS tile layout: token t's 16-byte chunk c (c in [0, 72)) lives at chunk
-// index t*72 + (c ^ swz(t)).  The XOR only touches the low three bits, so a
-// chunk stays inside its aligned group of eight.  swz(t) is a bijection over
-// each run of 8 tokens of equal parity and maps tokens 4v+k and 4v+k+2 to
-// values that differ above bit 0; with a row pitch of 72 chunks this makes
-//  - 16 consecutive tokens reading the same chunk (the K operand) hit 16
-//    distinct 16-byte bank groups of a 256-byte bank window, and
-//  - 4 consecutive tokens reading a 2-chunk column pair (the transposed V
-//    operand read) hit 8 distinct bank groups.
-__device__ __forceinline__ int swz(int t) {
-    int u = (t >> 1) & 7;
-    return ((u & 1) << 2) | (u >> 1);
+// LDS tile layout (32 tokens x 72 chunks of 16 bytes): chunk c of token t
+// lives at chunk index 32c + (t ^ f(c)), f(c) = 4(c & 1) + 8((c >> 1) & 1),
+// i.e. column-major with an XOR on the token.  Consequences:
+//  - a direct-to-LDS load instruction writes 64 consecutive chunks = columns
+//    2k and 2k+1, so lane l reads token (l & 31) ^ f(2k + (l >> 5)) and its
+//    source offset is a per-lane constant plus 32k bytes;
+//  - 16 lanes reading one column for 16 consecutive tokens (the K operand)
+//    touch 16 distinct 16-byte bank slots;
+//  - the transposed V read (4 tokens x 2 columns per 16 lanes, the next 16
+//    lanes two columns further) touches 16 distinct slots per 32 lanes.
+__device__ __forceinline__ int col_xor(int c) { return 4 * (c & 1) + 8 * ((c >> 1) & 1); }
+__device__ __forceinline__ int lds_chunk(int t, int c) { return 32 * c + (t ^ col_xor(c)); }
+
+// Load of a wave-uniform value through the constant address space: a scalar
+// load (s_load, counted by lgkmcnt), so waiting for it never waits for the
+// vector loads that stream KV tiles.  Only for memory the kernel never writes.
+template <class T>
+__device__ __forceinline__ T sload(const T* p) {
+    return *(const __attribute__((address_space(4))) T*)(p);
 }
-__device__ __forceinline__ int lds_chunk(int t, int c) { return t * kRowChunks + (c ^ swz(t)); }
 
 __device__ __forceinline__ int visible_len(int L, int s_q, int i, int causal) {
     if (!causal) return L;
@@ -85,6 +92,15 @@ struct RowResolver {
     }
     __device__ __forceinline__ int page(int j, int tile) const {
         return block_table[(int64_t)(j / s_q) * max_blocks + tile];
+    }
+    // wave-uniform variants (scalar loads)
+    __device__ __forceinline__ int slots_uniform(int j) const {
+        if (topk > 0) return topk;
+        int b = j / s_q, i = j - b * s_q;
+        return visible_len(clamp_len(sload(cache_seqlens + b), max_blocks), s_q, i, causal);
+    }
+    __device__ __forceinline__ int page_uniform(int j, int tile) const {
+        return sload(block_table + (int64_t)(j / s_q) * max_blocks + tile);
     }
     __device__ __forceinline__ int64_t row(int j, int slot, int nslots) const {
         if (slot >= nslots) return -1;

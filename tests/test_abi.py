@@ -52,17 +52,19 @@ def _problem(**kw):
 def test_plan_host_only():
     import mla_decode_amd as mla
     m = mla.plan(_problem(), num_cus=256)
-    assert m.num_head_blocks == 2 and m.num_partitions == 128 and m.fixed_overhead == 1
-    assert m.max_splits == 64 + 128
-    assert m.bytes == (8 + 5 * 128 + 64 + 1) * 4
-    assert mla.workspace_bytes(m) == 192 * 128 * 513 * 4
+    assert m.num_head_blocks == 1 and m.num_partitions == 256 and m.fixed_overhead == 1
+    assert m.max_splits == 64 + 256
+    assert m.bytes == (8 + 5 * 256 + 64 + 1) * 4
+    assert mla.workspace_bytes(m) == 320 * 128 * 513 * 4
+    m = mla.plan(_problem(h_q=192), num_cus=256)
+    assert m.num_head_blocks == 2 and m.num_partitions == 128
     m = mla.plan(_problem(h_q=16, batch=2, num_blocks=8, max_blocks_per_seq=4), num_cus=256)
     assert m.num_head_blocks == 1 and m.num_partitions == 256
 
 
 @pytest.mark.parametrize("kw,status", [
     (dict(batch=0), 1), (dict(s_q=0), 1), (dict(h_q=0), 1), (dict(num_blocks=0), 1),
-    (dict(max_blocks_per_seq=0), 1), (dict(topk=-1), 1), (dict(softmax_scale=float("nan")), 1),
+    (dict(max_blocks_per_seq=0), 1), (dict(topk=-1), 1), (dict(softmax_scale=float("nan")), 1), (dict(softmax_scale=0.0), 1), (dict(softmax_scale=-0.5), 1),
     (dict(topk=64, causal=True), 2), (dict(batch=20000), 2),
 ])
 def test_plan_rejects(kw, status):
