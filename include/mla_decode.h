@@ -120,7 +120,7 @@ mla_status_t mla_plan(const mla_problem_t *problem, int32_t num_cus, mla_metadat
  * max_splits * h_q * (512 + 1) float32.  0 if ``meta`` is NULL. */
 size_t mla_workspace_bytes(const mla_metadata_t *meta);
 
-/* a1: split-KV tile scheduler.  Writes meta->dev on ``stream`` from
+/* Split-KV tile scheduler.  Writes meta->dev on ``stream`` from
  * cache_seqlens (device, [batch]; ignored and may be NULL when topk > 0).
  * The scheduler balances KV tiles of 64 tokens (plus a fixed per-item cost)
  * over the partitions in contiguous ranges (FlashMLA new-kernel deep dive,
@@ -130,7 +130,7 @@ size_t mla_workspace_bytes(const mla_metadata_t *meta);
 mla_status_t mla_get_decode_metadata(const mla_problem_t *problem, const int32_t *cache_seqlens,
                                      mla_metadata_t *meta, void *stream);
 
-/* a2-a9, dense: decode over the paged cache through block_table and
+/* Dense decode over the paged cache through block_table and
  * cache_seqlens (both device).  problem->topk must be 0.  Writes out and lse.
  * ``workspace`` holds split partials (device, >= mla_workspace_bytes(meta)).
  * The caller keeps ``meta->dev`` current: reusing metadata made from other
@@ -141,7 +141,7 @@ mla_status_t mla_decode_fwd(const mla_problem_t *problem, const void *q, const v
                             const mla_metadata_t *meta, void *workspace, size_t workspace_bytes,
                             void *out, float *lse, void *stream);
 
-/* a2-a9, top-k sparse (DeepSeek Sparse Attention): each query token attends
+/* Top-k sparse decode (DeepSeek Sparse Attention): each query token attends
  * to the cache rows listed in indices[b, i, :] (device int32, page*64 +
  * offset; block_table is not used, FlashMLA README "indices Tensor").  Entries
  * < 0 or >= num_blocks*64 are masked (the pages mark -1 invalid and do no
@@ -152,7 +152,7 @@ mla_status_t mla_sparse_decode_fwd(const mla_problem_t *problem, const void *q, 
                                    void *workspace, size_t workspace_bytes,
                                    void *out, float *lse, void *stream);
 
-/* a9: LSE merge of split partials ("matrices, attention & GPU" explainer,
+/* LSE merge of split partials ("matrices, attention & GPU" explainer,
  * split-KV section: m = max(m1, m2), l = l1 e^(m1-m) + l2 e^(m2-m),
  * o = (o1 l1 e^(m1-m) + o2 l2 e^(m2-m)) / l).  Item j = b*s_q + i owns the
  * split slots [split_offsets[j], split_offsets[j+1]) of
@@ -165,7 +165,7 @@ mla_status_t mla_combine(int32_t num_items, int32_t h_q, int32_t s_q, const floa
                          const float *lse_part, const int32_t *split_offsets, int32_t out_dtype,
                          void *out, float *lse, void *stream);
 
-/* Test hook for a2: writes, for every item j and KV slot t < tiles_j*64, the
+/* Test hook for the row resolution: writes, for every item j and KV slot t < tiles_j*64, the
  * physical cache row the decode kernels read for that slot, or -1 where the
  * slot is masked; rows_out is device int32 [batch*s_q, row_stride] with
  * row_stride = 64*max_blocks_per_seq (dense) or 64*ceil(topk/64) (sparse);

@@ -70,7 +70,7 @@ def workspace_bytes(meta):
 
 
 def get_decode_metadata(problem, cache_seqlens, meta, meta_buf, stream=None):
-    """a1: fill ``meta_buf`` (device uint8/int32 tensor >= meta.bytes) with the schedule."""
+    """Split-KV scheduler: fill ``meta_buf`` (device uint8/int32 tensor >= meta.bytes) with the schedule."""
     lib = _lib.load()
     _need(meta_buf, "meta_buf", None)
     if meta_buf.numel() * meta_buf.element_size() < meta.bytes:
@@ -84,7 +84,7 @@ def get_decode_metadata(problem, cache_seqlens, meta, meta_buf, stream=None):
 
 
 def decode_fwd(problem, q, kv_cache, block_table, cache_seqlens, meta, workspace, out, lse, stream=None):
-    """a2-a9 dense decode (mla_decode_fwd)."""
+    """Dense paged decode (mla_decode_fwd)."""
     lib = _lib.load()
     _need(q, "q", torch.bfloat16)
     _need(kv_cache, "kv_cache", None)
@@ -100,7 +100,7 @@ def decode_fwd(problem, q, kv_cache, block_table, cache_seqlens, meta, workspace
 
 
 def sparse_decode_fwd(problem, q, kv_cache, indices, meta, workspace, out, lse, stream=None):
-    """a2-a9 top-k sparse decode (mla_sparse_decode_fwd)."""
+    """Top-k sparse decode (mla_sparse_decode_fwd)."""
     lib = _lib.load()
     _need(q, "q", torch.bfloat16)
     _need(kv_cache, "kv_cache", None)
@@ -114,7 +114,7 @@ def sparse_decode_fwd(problem, q, kv_cache, indices, meta, workspace, out, lse, 
 
 
 def combine(num_items, h_q, s_q, o_part, lse_part, split_offsets, out, lse, stream=None):
-    """a9 standalone LSE merge (mla_combine)."""
+    """Standalone LSE merge of split partials (mla_combine)."""
     lib = _lib.load()
     _need(o_part, "o_part", torch.float32)
     _need(lse_part, "lse_part", torch.float32)

@@ -1,4 +1,4 @@
-// a9: LSE merge of split partials, plus the a2 debug gather.
+// LSE merge of split partials, plus the debug gather of cache row ids.
 //
 // Combine: one workgroup per (item, 4 heads); 64 lanes x 8 dims cover the 512
 // output dims of a head.  With m* = max_k lse_k and w_k = exp(lse_k - m*):
@@ -62,7 +62,7 @@ hipError_t launch_combine(const CombineArgs& a, hipStream_t stream) {
     return hipGetLastError();
 }
 
-// a2 test hook: the rows the decode kernels read, through the same resolver.
+// Test hook: the rows the decode kernels read, through the same resolver.
 __global__ void __launch_bounds__(256) gather_kernel(const GatherArgs a) {
     const int j = blockIdx.x;
     const bool sparse = a.topk > 0;

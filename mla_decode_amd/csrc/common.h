@@ -63,7 +63,7 @@ __device__ __forceinline__ int clamp_len(int L, int max_blocks) {
     return L < 0 ? 0 : (L > cap ? cap : L);
 }
 
-// a2: physical cache row of a KV slot, or -1 if the slot is masked.
+// Physical cache row of a KV slot, or -1 if the slot is masked.
 // Dense: slot = logical token of request b, read through its page table; a
 // page id outside [0, num_blocks) masks its whole page.  Sparse: slot = top-k
 // entry holding page*64 + offset; entries < 0 or >= num_rows are masked.

@@ -1,4 +1,4 @@
-// a1: split-KV tile scheduler, one workgroup, integer arithmetic only.
+// Split-KV tile scheduler, one workgroup, integer arithmetic only.
 //
 // Items are query tokens (j = b*s_q + i) with n_j KV tiles of 64 tokens
 // (dense: causal-visible length; sparse: topk).  Each item costs n_j + F;

@@ -33,7 +33,7 @@ def _say(*a):
     print(*a, flush=True)
 
 
-# ------------------------------------------------------------------ a1: metadata
+# ------------------------------------------------------------------ scheduler metadata
 
 def _meta_case(w, num_cus):
     import mla_decode_amd as mla
@@ -68,7 +68,7 @@ def test_metadata_bit_exact_random(seed):
         _meta_case(w, num_cus)
 
 
-# ------------------------------------------------------------------ a2: gather rows
+# ------------------------------------------------------------------ gather rows
 
 def _gather_case(w, table):
     import mla_decode_amd as mla
@@ -196,7 +196,7 @@ def test_fp8_sparse_small():
     _say(compare(go, gl, ro, rl, rel_l2=FP8_REL_L2, max_abs=5e-2))
 
 
-# ------------------------------------------------------------------ a9: combine entry point
+# ------------------------------------------------------------------ combine entry point
 
 def test_combine_standalone():
     import mla_decode_amd as mla

@@ -144,6 +144,32 @@ def test_closed_forms():
     assert np.all(out == 0) and np.isneginf(lse[0])
 
 
+def test_decode_closed_forms_through_the_page_table():
+    """Worked example through ``decode``: one request whose two pages are 3 and
+    1 of a 4-page pool, with 65 visible tokens, is rows 192..255 then row 64.
+    A zero query then gives the mean of those rows' first 512 values and
+    lse = ln 65.  With one visible token (row 192) the output is that row's
+    first 512 values and lse is the scaled dot product over all 576 dims."""
+    rng = np.random.default_rng(11)
+    kv = torch.randn(4 * 64, 576, generator=torch.Generator().manual_seed(3)).to(torch.bfloat16)
+    kv_bits = _bits(kv)
+    kv64 = kv.double().numpy()
+    table = np.array([[3, 1]])
+    q = torch.zeros(1, 1, 2, 576, dtype=torch.bfloat16)
+    out, lse = A.decode(_bits(q), kv_bits, 0.05, block_table=table, cache_seqlens=np.array([65]))
+    rows = list(range(192, 256)) + [64]
+    want = kv64[rows, :512].mean(axis=0)
+    assert np.max(np.abs(out[0, 0, 0] - want)) < 1e-12
+    assert np.max(np.abs(out[0, 0, 1] - want)) < 1e-12
+    assert np.all(np.abs(lse[0, :, 0] - math.log(65)) < 1e-12)
+    qr = torch.from_numpy(rng.standard_normal((1, 1, 2, 576))).to(torch.bfloat16)
+    out, lse = A.decode(_bits(qr), kv_bits, 0.05, block_table=table, cache_seqlens=np.array([1]))
+    q64 = qr.double().numpy()[0, 0]
+    for h in range(2):
+        assert np.max(np.abs(out[0, 0, h] - kv64[192, :512])) < 1e-15
+        assert abs(lse[0, h, 0] - 0.05 * float(q64[h] @ kv64[192])) < 1e-12
+
+
 def test_absorption_identity():
     """Non-absorbed MHA with per-head up-projections equals W^UV applied to the
     oracle run on the latent cache with the absorbed query."""
