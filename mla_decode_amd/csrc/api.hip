@@ -14,7 +14,7 @@ namespace {
 
 using mla::kBlock;
 
-constexpr int kFixedOverhead = 1;
+constexpr int kFixedOverhead = 0;
 constexpr int kMaxDevices = 64;
 
 int g_cu_count[kMaxDevices];

@@ -3,14 +3,14 @@
 // One workgroup = 128 query heads x one scheduler partition (a contiguous run
 // of 64-token KV pages, possibly spanning several items), so every cache page
 // is read from HBM once per query token.  Eight waves, two per SIMD, 256
-// registers each; wave w owns head block hb = w & 3 (32 heads) and half
-// kh = w >> 2.  Each page is computed as two 32-token tiles:
+// registers each; wave w owns head block hb = w >> 1 (32 heads) and half
+// kh = w & 1.  Each page is computed as two 32-token tiles:
 //
 //   fill   tiles are copied global -> LDS with 16-byte buffer loads that
-//          write LDS directly (bf16 cache; two tiles in flight, three LDS
-//          buffers), or loaded to registers, dequantised and stored (FP8
-//          cache).  Masked tokens fall outside the buffer range and land as
-//          zeros;
+//          write LDS directly (bf16 cache; three LDS buffers: the tile being
+//          multiplied, the previous one for PV, the next one landing), or
+//          loaded to registers, dequantised and stored (FP8 cache).  Masked
+//          tokens fall outside the buffer range and land as zeros;
 //   QK     the two waves of a head block split the 576 dims: wave kh runs
 //          S^T = K Q^T over latent dims 256*kh.. and half of the RoPE dims
 //          with v_mfma_f32_32x32x16_bf16 (Q in registers, RoPE part of Q in
@@ -18,10 +18,16 @@
 //          on the MFMA rows, so each lane holds one head's scores;
 //   soft   both waves of a head block run the same exact online softmax
 //          (running max updated on every increase, p = exp2(s*c - m) in fp32,
-//          l sums the fp32 p, P rounded to bf16 for the PV product);
+//          l sums the fp32 p, P rounded to bf16 for the PV product) and
+//          rescale their part of O;
 //   PV     wave kh accumulates O^T for dims 256*kh.. of its 32 heads; the
 //          transposed V operand is read straight from the row-major LDS tile
 //          with ds_read_b64_tr_b16 and P^T is the wave's own S^T registers.
+//
+// The waves form two groups (0-3 and 4-7, one wave of each per SIMD) that run
+// the same step sequence one step apart: while one group issues the MFMAs of
+// PV and QK, the other runs the softmax, so the matrix and vector units of a
+// SIMD work at the same time.
 //
 // Items whose KV range sits in one partition write out/lse directly; split
 // items write normalised fp32 partials for the combine kernel.
@@ -34,15 +40,33 @@ namespace mla {
 constexpr int kSubBytes = kSubTok * kRowBytes;   // 36864
 constexpr int kNBuf = 3;
 
+template <int V>
+struct IntC {
+    static constexpr int value = V;
+};
+
+// The small arrays come first: LDS instructions encode at most a 16-bit
+// immediate offset, so arrays addressed with many constant offsets must sit
+// below 64 KiB to share one address register.
 struct __attribute__((aligned(16))) Smem {
-    unsigned char tile[kNBuf][kSubBytes];   // 32-token KV tiles (bf16, swizzled)
     f32x4 xs[4][2][4][64];                  // partial S^T [head block][dim half][register quad][lane]
     bf16x8 qr[4][4][64];                    // RoPE part of Q as B fragments [head block][k-step][lane]
     int rows[4][kSubTok];                   // sparse: row ids of upcoming tiles (ring of 4)
+    unsigned char tile[kNBuf][kSubBytes];   // 32-token KV tiles (bf16, swizzled)
 };
 
 __device__ __forceinline__ bf16x4 tr_read(const unsigned char* p) {
     return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((__attribute__((address_space(3))) bf16x4*)(p));
+}
+
+// Byte offset of LDS tile buffer ``idx``, hidden from the optimiser so that it
+// does not precompute one set of lane addresses per buffer (addresses above
+// 64 KiB cannot use the instruction's immediate offset and would each hold a
+// register); each step adds the uniform offset to a few lane bases instead.
+__device__ __forceinline__ int opaque_tile_offset(int idx) {
+    int off = idx * (kSubTok * kRowBytes);
+    __asm__ volatile("" : "+s"(off));
+    return off;
 }
 
 __device__ __forceinline__ bf16x8 pack8(const float* v) {
@@ -52,8 +76,39 @@ __device__ __forceinline__ bf16x8 pack8(const float* v) {
     return r;
 }
 
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, int stride, int num_records) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)stride, num_records, 0x00020000);
+// Buffer resource for untyped loads: base, stride (bytes, struct loads only),
+// num_records (bytes for raw loads, records for struct loads; accesses beyond
+// it return zeros), 32-bit data format.  Built from uniform values, so it
+// lives in scalar registers.
+__device__ __forceinline__ i32x4 buffer_rsrc(const void* base, int stride, int num_records) {
+    const uint64_t p = (uint64_t)base;
+    i32x4 r;
+    r[0] = (int)(uint32_t)p;
+    r[1] = (int)(((uint32_t)(p >> 32) & 0xffffu) | ((uint32_t)stride << 16));
+    r[2] = num_records;
+    r[3] = 0x00020000;
+    return r;
+}
+
+// 16-byte-per-lane global -> LDS copies (one wave instruction writes 1 KiB of
+// LDS at M0).  They are issued through inline assembly so that the compiler
+// does not treat them as pending LDS stores: it would otherwise wait for every
+// in-flight tile load before the next LDS read of any other tile.  The kernel
+// orders them itself: s_waitcnt vmcnt(0) by every wave, then a workgroup
+// barrier, before a filled tile is read.
+// The immediate offset moves both the global source and the LDS destination
+// (LDS address = M0 + offset + 16 * lane), so M0 is set to the destination
+// minus the immediate.
+template <int IMM>
+__device__ __forceinline__ void dma_raw_x4(const i32x4& rs, int voff, int lds) {
+    __asm__ volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen offset:%3 lds"
+                     :: "s"(lds - IMM), "v"(voff), "s"(rs), "i"(IMM) : "memory", "m0");
+}
+template <int IMM>
+__device__ __forceinline__ void dma_struct_x4(const i32x4& rs, int row, int voff, int lds) {
+    const i32x2 va = {row, voff};
+    __asm__ volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 idxen offen offset:%3 lds"
+                     :: "s"(lds - IMM), "v"(va), "s"(rs), "i"(IMM) : "memory", "m0");
 }
 
 // ---- bf16 tile fill: 36 pieces of 1 KB = LDS columns 2k, 2k+1; wave w issues
@@ -63,31 +118,30 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, 
 __device__ __forceinline__ int fill_loads(int wave) { return wave < 4 ? 5 : 4; }
 
 // dense: the tile is one half of a 64-token page; tokens >= tok_valid are masked
-__device__ __forceinline__ void fill_dense(unsigned char* dst, const unsigned char* kv, int page, int sub,
+// ``dst`` is the LDS byte address of the tile buffer.
+__device__ __forceinline__ void fill_dense(int dst, const unsigned char* kv, int page, int sub,
                                            int tok_valid, int64_t num_rows, int fbase, int wave) {
     const bool ok = page_ok(page, num_rows);
     int nvalid = tok_valid < kSubTok ? tok_valid : kSubTok;
     if (!ok || nvalid < 0) nvalid = 0;
     const unsigned char* base = kv + (ok ? (int64_t)page * kTileBytes + sub * kSubBytes : 0);
-    const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(base, 0, nvalid * kRowBytes);
-#pragma unroll
-    for (int i = 0; i < 5; ++i) {
-        if (i == 4 && wave >= 4) break;
-        const int k = i < 4 ? wave + 8 * i : 32 + wave;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t*)(dst + k * 1024), 16, fbase + 32 * k, 0, 0, 0);
-    }
+    const i32x4 rs = buffer_rsrc(base, 0, nvalid * kRowBytes);
+    const int l0 = dst + wave * 1024;
+    dma_raw_x4<0>(rs, fbase + 32 * wave, l0);
+    dma_raw_x4<256>(rs, fbase + 32 * wave, l0 + 8 * 1024);
+    dma_raw_x4<512>(rs, fbase + 32 * wave, l0 + 16 * 1024);
+    dma_raw_x4<768>(rs, fbase + 32 * wave, l0 + 24 * 1024);
+    if (wave < 4) dma_raw_x4<0>(rs, fbase + 32 * (32 + wave), l0 + 32 * 1024);
 }
 
 // sparse: the lane's row id from the LDS ring (-1 = masked -> index out of range)
-__device__ __forceinline__ void fill_sparse(unsigned char* dst, __amdgpu_buffer_rsrc_t rs, int row, int fcol,
-                                            int wave) {
-#pragma unroll
-    for (int i = 0; i < 5; ++i) {
-        if (i == 4 && wave >= 4) break;
-        const int k = i < 4 ? wave + 8 * i : 32 + wave;
-        __builtin_amdgcn_struct_ptr_buffer_load_lds(rs, (lds_void_t*)(dst + k * 1024), 16, (unsigned)row,
-                                                    fcol + 32 * k, 0, 0, 0);
-    }
+__device__ __forceinline__ void fill_sparse(int dst, const i32x4& rs, int row, int fcol, int wave) {
+    const int l0 = dst + wave * 1024;
+    dma_struct_x4<0>(rs, row, fcol + 32 * wave, l0);
+    dma_struct_x4<256>(rs, row, fcol + 32 * wave, l0 + 8 * 1024);
+    dma_struct_x4<512>(rs, row, fcol + 32 * wave, l0 + 16 * 1024);
+    dma_struct_x4<768>(rs, row, fcol + 32 * wave, l0 + 24 * 1024);
+    if (wave < 4) dma_struct_x4<0>(rs, row, fcol + 32 * (32 + wave), l0 + 32 * 1024);
 }
 
 // ---- FP8 tile fill: thread (token t = tid/16, part p = tid%16) owns latent
@@ -152,14 +206,68 @@ __device__ __forceinline__ void wait_vm(int n) {
     else __builtin_amdgcn_s_waitcnt(0x0F70);
 }
 
+// Instruction order of the MFMA step, pinned for the scheduler: the LDS
+// reads of operations I0 and I0+1 first, then each MFMA followed by the reads
+// of the operation two ahead (two for a PV step or a RoPE step, one for a
+// latent QK step), then the four stores of the partial scores.
+constexpr int kSchedValu = 0x002, kSchedMfma = 0x008, kSchedDsRead = 0x100, kSchedDsWrite = 0x200;
+constexpr int kMstepLookahead = 3;   // operations whose operands are in flight
+constexpr int mstep_reads(int i) { return (i < 16 || i >= 32) ? 2 : 1; }
+
+template <int B, int E, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+    if constexpr (B < E) {
+        f(IntC<B>{});
+        static_for<B + 1, E>(f);
+    }
+}
+
+template <int I, int I1>
+__device__ __forceinline__ void mstep_schedule() {
+    if constexpr (I < I1) {
+        __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+        if constexpr (I + kMstepLookahead < I1)
+            __builtin_amdgcn_sched_group_barrier(kSchedDsRead, mstep_reads(I + kMstepLookahead), 0);
+        mstep_schedule<I + 1, I1>();
+    }
+}
+
+template <int I, int I1>
+constexpr int mstep_first_reads() {
+    if constexpr (I < I1) return mstep_reads(I) + mstep_first_reads<I + 1, (I1 < I + kMstepLookahead ? I1 : I + kMstepLookahead)>();
+    else return 0;
+}
+
+template <int I0, int I1>
+__device__ __forceinline__ void mstep_schedule_all() {
+    constexpr int first = mstep_first_reads<I0, (I1 < I0 + kMstepLookahead ? I1 : I0 + kMstepLookahead)>();
+    __builtin_amdgcn_sched_group_barrier(kSchedDsRead, first, 0);
+    mstep_schedule<I0, I1>();
+    if constexpr (I1 == 34) __builtin_amdgcn_sched_group_barrier(kSchedDsWrite, 4, 0);
+}
+
+// A tile copy to be issued piecewise: buffer resource, sparse row id, lane
+// source offset and LDS address of the wave's first piece.
+struct FillCtx {
+    bool on;
+    i32x4 rs;
+    int row, vo, l0;
+};
+
 template <bool SPARSE, bool FP8>
 __global__ void __launch_bounds__(kThreads, 1) decode_kernel(const DecodeArgs a) {
     __shared__ Smem sm;
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int hb = wave & 3;          // head block: heads 32*hb .. +31 of the workgroup
-    const int kh = wave >> 2;         // half: QK dims and PV output dims
+    // Two groups of four waves run the same step sequence one step apart
+    // (group 1 lags).  The dispatcher puts wave w on SIMD w % 4, so every SIMD
+    // hosts one wave of each group: while one runs MFMA work the other runs
+    // VALU work.  Waves w and w^1 (same group, different SIMDs) share head
+    // block hb and exchange partial scores.
+    const int grp = wave >> 2;
+    const int hb = wave >> 1;         // head block: heads 32*hb .. +31 of the workgroup
+    const int kh = wave & 1;          // half: QK dims and PV output dims
     const int l32 = lane & 31;
     const int half = lane >> 5;
 
@@ -192,7 +300,7 @@ __global__ void __launch_bounds__(kThreads, 1) decode_kernel(const DecodeArgs a)
     const int head = hblk * kHeadsPerWG + hb * 32 + l32;   // this lane's head
     const bool head_ok = head < H;
 
-    const __amdgpu_buffer_rsrc_t srs = buffer_rsrc(kv, kRowBytes, (int)a.num_rows);
+    const i32x4 srs = buffer_rsrc(kv, kRowBytes, (int)a.num_rows);
     const int f8_tok = tid >> 4, f8_p = tid & 15;    // FP8 fill role
     const int nload = fill_loads(wave);
     const int ftok = l32 ^ (4 * half + 8 * (wave & 1));   // bf16 fill: token this lane copies
@@ -260,7 +368,21 @@ __global__ void __launch_bounds__(kThreads, 1) decode_kernel(const DecodeArgs a)
         float m_run = -INFINITY, l_run = 0.f;
 
         // dense: page ids of tiles it, it+1, it+2 (one 64-token page = two tiles)
-        auto page_of = [&](int g) { return rr.page_uniform(j, g >> 1); };
+        // dense: page ids of 64 consecutive pages of item j, one per lane, read
+        // with v_readlane.  A scalar load here would be waited for with
+        // lgkmcnt(0), which also drains every outstanding LDS operation.
+        const int b_item = j / a.s_q;
+        const int npages_item = (nslots + kBlock - 1) / kBlock;
+        int pt_base = g0 >> 1, pt_v = 0;
+        auto load_pages = [&](int first) __attribute__((always_inline)) {
+            pt_base = first;
+            const int pi = first + lane;
+            pt_v = pi < npages_item ? a.block_table[(int64_t)b_item * a.max_blocks + pi] : 0;
+        };
+        if (!SPARSE) load_pages(g0 >> 1);
+        auto page_of = [&](int g) __attribute__((always_inline)) {
+            return __builtin_amdgcn_readlane(pt_v, (g >> 1) - pt_base);
+        };
         int pg0 = 0, pg1 = 0, pg2 = 0;
         if (!SPARSE) {
             pg0 = page_of(g0);
@@ -269,168 +391,307 @@ __global__ void __launch_bounds__(kThreads, 1) decode_kernel(const DecodeArgs a)
         }
         if (SPARSE && wave == 0 && lane < kSubTok) {
 #pragma unroll
-            for (int u = 0; u < 3; ++u)
+            for (int u = 0; u < 2; ++u)
                 if (u < ns) sm.rows[u][lane] = (int)rr.row(j, (g0 + u) * kSubTok + lane, nslots);
         }
         lds_barrier();
 
-        auto issue_fill = [&](int it, int page) {
+        auto issue_fill = [&](int it, int page) __attribute__((always_inline)) {
             const int g = g0 + it;
-            unsigned char* dst = sm.tile[it % kNBuf];
+            const int dst = (int)(size_t)(lds_void_t*)&sm.tile[0][0] + opaque_tile_offset(it % kNBuf);
             if (SPARSE) fill_sparse(dst, srs, sm.rows[it & 3][ftok], fcol, wave);
             else fill_dense(dst, kv, page, g & 1, nslots - g * kSubTok, a.num_rows, fbase, wave);
         };
         Fp8Regs f8;
-        auto fp8_row = [&](int it, int page) -> int64_t {
+        auto fp8_row = [&](int it, int page) __attribute__((always_inline)) -> int64_t {
             const int g = g0 + it;
             if (SPARSE) return sm.rows[it & 3][f8_tok];
             return row_in_page(page, (g & 1) * kSubTok + f8_tok, nslots - (g & ~1) * kSubTok, a.num_rows);
         };
+        // tile 0 lands before step 0
         if (FP8) {
             fp8_load(f8, kv, fp8_row(0, pg0), f8_p);
             fp8_store(sm.tile[0], f8, f8_tok, f8_p);
         } else {
             issue_fill(0, pg0);
-            if (ns > 1) issue_fill(1, pg1);
+            __builtin_amdgcn_s_waitcnt(0x0F70);
         }
+        lds_barrier();
 
-        for (int it = 0; it < ns; ++it) {
-            const int g = g0 + it;
-            const unsigned char* T = sm.tile[it % kNBuf];
-            if (!FP8) wait_vm(it + 1 < ns ? nload : 0);
-            lds_barrier();                                 // tile it ready; tile it-1 finished everywhere
+        // ---- step pipeline ----
+        // Per tile t a wave runs an MFMA step M(t) = PV(t-1), QK(t) and a VALU
+        // step V(t) = partner exchange, online softmax of tile t and rescale of O;
+        // M(ns) is the last PV alone.  Group 0 runs M(t), V(t) in steps 2t,
+        // 2t+1; group 1 runs V(t-1), M(t), so on every SIMD one wave issues
+        // MFMAs while the other runs the softmax.  Tile t is read in steps
+        // 2t..2t+3.  Group 1 copies tile t+1 into the buffer of tile t-2 at the
+        // start of step 2t; every wave waits for its copies at the end of step
+        // 2t+1.  Every step ends with a workgroup barrier.  The
+        // group is a compile-time constant so that each wave's step sequence is
+        // straight-line code.
+        f32x16 s = {};
+        bf16x8 p0 = {}, p1 = {};
 
-            // sparse: row ids of tile it+3 (issued before the fills so that waiting
-            // for them never waits for a tile)
-            int next_row = -1;
-            if (SPARSE && wave == 0 && lane < kSubTok && it + 3 < ns)
-                next_row = (int)rr.row(j, (g + 3) * kSubTok + lane, nslots);
-            // keep the pipeline full: tile it+2 (bf16) or it+1 (FP8) in flight
-            if (FP8) {
-                if (it + 1 < ns) fp8_load(f8, kv, fp8_row(it + 1, pg1), f8_p);
-            } else if (it + 2 < ns) {
-                issue_fill(it + 2, pg2);
-            }
-            const int pg_cur = pg0;
-            if (!SPARSE) {
-                pg0 = pg1;
-                pg1 = pg2;
-                pg2 = it + 3 < ns ? page_of(g + 3) : 0;
-            }
-
-            // ---- QK: partial S^T[32 tokens x 32 heads] over this wave's dims ----
-            f32x16 s = {};
-            const unsigned char* Tk = T + 16384 * kh;
+        // MFMA step body: PV(t-1) (16 MFMAs) then QK(t) (18 MFMAs), as one
+        // sequence of operations whose LDS operands are fetched kMstepLookahead
+        // ahead.  Operation i < 16 is PV k-step i/8 for output block i%8; operation 16 + k is
+        // QK k-step k (k < 16 latent dims of this half, then two RoPE k-steps
+        // whose Q fragment also comes from LDS).  P and S are never live
+        // together.
+        auto mstep = [&](int t, auto pv_c, auto qk_c) __attribute__((always_inline)) {
+            constexpr bool DO_PV = decltype(pv_c)::value != 0;
+            constexpr bool DO_QK = decltype(qk_c)::value != 0;
+            constexpr int I0 = DO_PV ? 0 : 16;
+            constexpr int I1 = DO_QK ? 34 : 16;
+            const unsigned char* Tp = sm.tile[0] + opaque_tile_offset((t + kNBuf - 1) % kNBuf) + 16384 * kh;  // t-1
+            const unsigned char* T = sm.tile[0] + opaque_tile_offset(t % kNBuf);                               // t
+            auto fetch = [&](int i, bf16x8& A, bf16x8& B) __attribute__((always_inline)) {
+                if (i < 16) {
+                    const unsigned char* Tv = Tp + 256 * (i >> 3) + 2048 * (i & 7);
+                    const bf16x4 v0 = tr_read(Tv + vb[0]);
+                    const bf16x4 v1 = tr_read(Tv + vb[1]);
+                    A = bf16x8{v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+                } else if (i < 32) {
+                    const int kk = i - 16;
+                    A = *(const bf16x8*)(T + 16384 * kh + kb[kk & 1] + 1024 * kk);
+                } else {
+                    const int kr = 2 * kh + (i - 32);    // RoPE column 64 + 2kr + half
+                    A = *(const bf16x8*)(T + 32768 + kb[kr & 1] + 1024 * kr);
+                    B = sm.qr[hb][kr][lane];
+                }
+            };
+            constexpr int LA = kMstepLookahead;
+            bf16x8 opA[LA + 1], opB[LA + 1];
 #pragma unroll
-            for (int kk = 0; kk < 16; ++kk) {
-                const bf16x8 kf = *(const bf16x8*)(Tk + kb[kk & 1] + 1024 * kk);
-                s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[kk], s, 0, 0, 0);
-            }
-#pragma unroll
-            for (int r2 = 0; r2 < 2; ++r2) {
-                const int kr = 2 * kh + r2;     // RoPE column 64 + 2kr + half
-                const bf16x8 kf = *(const bf16x8*)(T + 32768 + kb[kr & 1] + 1024 * kr);
-                const bf16x8 qv = sm.qr[hb][kr][lane];
-                s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qv, s, 0, 0, 0);
-            }
-#pragma unroll
-            for (int i = 0; i < 4; ++i) sm.xs[hb][kh][i][lane] = f32x4{s[4 * i], s[4 * i + 1], s[4 * i + 2], s[4 * i + 3]};
-            lds_barrier();
-
-            // ---- full scores: own + partner partial; mask; scale (in place) ----
-            // register r -> token 8(r/4) + 4*half + r%4 of the tile
-            {
-                const int tv = nslots - g * kSubTok;
-                const bool pg = SPARSE ? true : page_ok(pg_cur, a.num_rows);
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const f32x4 o = sm.xs[hb][kh ^ 1][i][lane];
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const int tok = 8 * i + 4 * half + e;
-                        const bool valid = SPARSE ? (sm.rows[it & 3][tok] >= 0) : (pg && tok < tv);
-                        s[4 * i + e] = valid ? (s[4 * i + e] + o[e]) * c : -INFINITY;
+            for (int i = I0; i < I0 + LA && i < I1; ++i) fetch(i, opA[i % (LA + 1)], opB[i % (LA + 1)]);
+            static_for<0, 34>([&](auto i_c) __attribute__((always_inline)) {
+                constexpr int i = decltype(i_c)::value;
+                if constexpr (i >= I0 && i < I1) {
+                    if (i + LA < I1) fetch(i + LA, opA[(i + LA) % (LA + 1)], opB[(i + LA) % (LA + 1)]);
+                    constexpr int r = i % (LA + 1);
+                    if constexpr (i < 16) {
+                        acc[i & 7] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(opA[r], (i < 8) ? p0 : p1, acc[i & 7],
+                                                                            0, 0, 0);
+                    } else if constexpr (i == 16) {
+                        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(opA[r], qf[0], f32x16{}, 0, 0, 0);
+                    } else if constexpr (i < 32) {
+                        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(opA[r], qf[i - 16], s, 0, 0, 0);
+                    } else {
+                        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(opA[r], opB[r], s, 0, 0, 0);
                     }
                 }
+            });
+            if (DO_QK) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    sm.xs[hb][kh][i][lane] = f32x4{s[4 * i], s[4 * i + 1], s[4 * i + 2], s[4 * i + 3]};
             }
-
-            // ---- exact online softmax over the tile's 32 tokens ----
+            mstep_schedule_all<I0, I1>();
+        };
+        // Copy of tile t+1 into the buffer of tile t-2, issued by group 1 during
+        // its softmax step 2t: wave 4 + w issues the nine 1-KiB pieces w + 4i,
+        // spread over the softmax so that the copies never queue up at once.
+        // With no tile left to copy the pieces still run, on an empty buffer
+        // range: they write zeros into the buffer of tile t-2, which no step
+        // reads any more.  Keeping them unconditional keeps the softmax step one
+        // basic block (a branch around each piece makes the compiler wait for
+        // every outstanding copy before the next one).
+        auto fill_prepare = [&](int t) __attribute__((always_inline)) -> FillCtx {
+            FillCtx f{true, {0, 0, 0, 0}, -1, 0, 0};
+            const int g = g0 + t + 1;
+            const int w = wave - 4;
+            const bool live = t + 1 < ns;
+            f.l0 = (int)(size_t)(lds_void_t*)&sm.tile[0][0] + opaque_tile_offset((t + 1) % kNBuf) + 1024 * w;
+            if (SPARSE) {
+                f.rs = srs;
+                f.row = live ? sm.rows[(t + 1) & 3][ftok] : -1;
+                f.vo = fcol + 32 * w;
+            } else if (!live) {
+                f.rs = buffer_rsrc(kv, 0, 0);
+                f.vo = fbase + 32 * w;
+            } else {
+                const bool ok = page_ok(pg1, a.num_rows);
+                int nvalid = min(nslots - g * kSubTok, kSubTok);
+                if (!ok || nvalid < 0) nvalid = 0;
+                f.rs = buffer_rsrc(kv + (ok ? (int64_t)pg1 * kTileBytes + (g & 1) * kSubBytes : 0), 0,
+                                   nvalid * kRowBytes);
+                f.vo = fbase + 32 * w;
+            }
+            return f;
+        };
+        auto fill_piece = [&](const FillCtx& f, auto i_c) __attribute__((always_inline)) {
+            constexpr int i = decltype(i_c)::value;
+            if (f.on) {
+                if (SPARSE) dma_struct_x4<128 * i>(f.rs, f.row, f.vo, f.l0 + 4096 * i);
+                else dma_raw_x4<128 * i>(f.rs, f.vo, f.l0 + 4096 * i);
+            }
+        };
+        const FillCtx nofill{false, {0, 0, 0, 0}, 0, 0, 0};
+        // full scores, mask, exact online softmax.  Register r holds token
+        // 8(r/4) + 4*half + r%4 of the tile.  Scores stay unscaled; c > 0 is
+        // folded into the exponent.
+        auto soft = [&](int t, const FillCtx& fc_in, auto fill_c) __attribute__((always_inline)) {
+            // ``on`` is a compile-time constant here, so the pieces are straight-line code
+            FillCtx fc = fc_in;
+            fc.on = decltype(fill_c)::value != 0 && !FP8;
+            const int g = g0 + t;
+            const int tv = nslots - g * kSubTok;
+            const int pg_t = SPARSE ? 0 : page_of(g);
+            const bool full = SPARSE ? false : (page_ok(pg_t, a.num_rows) && tv >= kSubTok);
+            f32x4 xo[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) xo[i] = sm.xs[hb][kh ^ 1][i][lane];
+            fill_piece(fc, IntC<0>{});
+            fill_piece(fc, IntC<1>{});
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) s[4 * i + e] += xo[i][e];
+            }
+            if (!full) {
+                // token 8(r/4) + 4 half + r%4 is valid iff 4 half < tv - 8(r/4) - r%4:
+                // one per-lane value against a uniform limit per register
+                const int tv_ok = SPARSE ? 0 : (page_ok(pg_t, a.num_rows) ? tv : 0);
+                const int h4 = 4 * half;
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int c_r = 8 * (r >> 2) + (r & 3);
+                    const bool valid = SPARSE ? (sm.rows[t & 3][h4 + c_r] >= 0) : (h4 < tv_ok - c_r);
+                    if (!valid) s[r] = -INFINITY;
+                }
+            }
             float mx = -INFINITY;
 #pragma unroll
             for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[r]);
             mx = wave_max_pair(mx);
+            fill_piece(fc, IntC<2>{});
+            fill_piece(fc, IntC<3>{});
             const float m_new = fmaxf(m_run, mx);
-            float alpha = 1.f, psum = 0.f;
-            if (m_new == -INFINITY) {
-                s = f32x16{};
-            } else {
-                alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    s[r] = __builtin_amdgcn_exp2f(s[r] - m_new);
-                    psum += s[r];
-                }
-            }
+            // while every score so far is masked, m_new = -inf: p = exp2(-inf) = 0
+            const float cm = m_new == -INFINITY ? 0.f : c * m_new;
+            const float alpha = __builtin_amdgcn_exp2f(c * m_run - cm);
+            float psum = 0.f;
+            static_for<0, 16>([&](auto r_c) __attribute__((always_inline)) {
+                constexpr int r = decltype(r_c)::value;
+                s[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c, -cm));
+                psum += s[r];
+                if constexpr (r == 5) fill_piece(fc, IntC<4>{});
+                if constexpr (r == 10) fill_piece(fc, IntC<5>{});
+                if constexpr (r == 15) fill_piece(fc, IntC<6>{});
+            });
             psum = wave_sum_pair(psum);
+            // rescale O (lane l holds head l%32); skipped when no head's max rose.
+            // O is zero until the first finite max, so it needs no rescale then.
+            const uint32_t rose = (uint32_t)__builtin_amdgcn_ballot_w64(alpha != 1.f);
+            if (rose != 0 && __builtin_amdgcn_ballot_w64(m_run != -INFINITY) != 0) {
+#pragma unroll
+                for (int dd = 0; dd < 8; ++dd)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) acc[dd][r] *= alpha;
+            }
+            fill_piece(fc, IntC<7>{});
             l_run = l_run * alpha + psum;
             m_run = m_new;
-            bf16x8 p0, p1;
 #pragma unroll
             for (int e = 0; e < 8; ++e) { p0[e] = (__bf16)s[e]; p1[e] = (__bf16)s[8 + e]; }
+            fill_piece(fc, IntC<8>{});
+        };
+        // step 2t: FP8 tile t+1 to registers; sparse row ids of tile t+2
+        auto step_even_begin = [&](int t) __attribute__((always_inline)) -> int {
+            int next_row = -1;
+            if (SPARSE && wave == 0 && lane < kSubTok && t + 2 < ns)
+                next_row = (int)rr.row(j, (g0 + t + 2) * kSubTok + lane, nslots);
+            if (FP8 && t + 1 < ns) fp8_load(f8, kv, fp8_row(t + 1, pg1), f8_p);
+            return next_row;
+        };
+        auto step_even_end = [&](int t, int next_row) __attribute__((always_inline)) {
+            if (SPARSE && wave == 0 && lane < kSubTok && t + 2 < ns) sm.rows[(t + 2) & 3][lane] = next_row;
+            lds_barrier();
+        };
+        // end of step 2t+1: tile t+1 has landed
+        auto step_odd_end = [&](int t) __attribute__((always_inline)) {
+            if (t + 1 < ns) {
+                if (FP8) fp8_store(sm.tile[0] + opaque_tile_offset((t + 1) % kNBuf), f8, f8_tok, f8_p);
+                else __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's tile copies
+            }
+            if (!SPARSE) {
+                if (((g0 + t + 3) >> 1) - pt_base >= 64) load_pages((g0 + t) >> 1);
+                pg1 = pg2;
+                pg2 = t + 3 < ns ? page_of(g0 + t + 3) : 0;
+            }
+            lds_barrier();
+        };
 
-            // ---- PV: O^T[dims 256kh + 32d .., heads] = alpha O^T + V^T P^T ----
-            if (__builtin_amdgcn_ballot_w64(alpha != 1.f) != 0) {
-#pragma unroll
-                for (int d = 0; d < 8; ++d) {
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) acc[d][r] *= alpha;
+        auto run = [&](auto grp_c) __attribute__((always_inline)) {
+            constexpr int G = decltype(grp_c)::value;
+            const IntC<0> no;
+            const IntC<1> yes;
+            // steps 0, 1
+            int nr = step_even_begin(0);
+            if (G == 0) {
+                mstep(0, no, yes);
+            } else {
+                if (!FP8) {
+                    const FillCtx fc = fill_prepare(0);
+                    static_for<0, 9>([&](auto i_c) __attribute__((always_inline)) { fill_piece(fc, i_c); });
                 }
             }
-#pragma unroll
-            for (int j2 = 0; j2 < 2; ++j2) {
-                const bf16x8 pf = j2 == 0 ? p0 : p1;
-                const unsigned char* Tv = T + 256 * j2 + 16384 * kh;
-#pragma unroll
-                for (int d = 0; d < 8; ++d) {
-                    const bf16x4 v0 = tr_read(Tv + vb[0] + 2048 * d);
-                    const bf16x4 v1 = tr_read(Tv + vb[1] + 2048 * d);
-                    const bf16x8 vf = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
-                    acc[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf, acc[d], 0, 0, 0);
-                }
+            step_even_end(0, nr);
+            if (G == 0) soft(0, nofill, no);
+            else mstep(0, no, yes);
+            step_odd_end(0);
+            // steady state: steps 2t, 2t+1
+            for (int t = 1; t < ns; ++t) {
+                nr = step_even_begin(t);
+                if (G == 0) mstep(t, yes, yes);
+                else soft(t - 1, fill_prepare(t), yes);
+                step_even_end(t, nr);
+                if (G == 0) soft(t, nofill, no);
+                else mstep(t, yes, yes);
+                step_odd_end(t);
             }
-
-            if (FP8 && it + 1 < ns) fp8_store(sm.tile[(it + 1) % kNBuf], f8, f8_tok, f8_p);
-            if (SPARSE && wave == 0 && lane < kSubTok && it + 3 < ns) sm.rows[(it + 3) & 3][lane] = next_row;
-        }
+            // drain: steps 2ns, 2ns+1 (the last tile's PV)
+            if (G == 0) mstep(ns, yes, no);
+            else soft(ns - 1, nofill, no);
+            lds_barrier();
+            if (G == 1) mstep(ns, yes, no);
+            lds_barrier();
+        };
+        if (grp == 0) run(IntC<0>{});
+        else run(IntC<1>{});
 
         // ---- epilogue: both waves of a head block hold the same m, l ----
+        // acc[d] register r, lane l: head 32-block base + l%32, dim 256 kh + 32 d +
+        // (r/4)*8 + 4*half + r%4 (four consecutive dims per register quad).
         const bool final_out = (nsplit == 1);
         const int b = j / a.s_q, iq = j - b * a.s_q;
-        if (head_ok && (final_out || (slot >= 0 && slot < a.max_slots))) {
+        if (final_out || (slot >= 0 && slot < a.max_slots)) {
             const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
+            if (head_ok) {
 #pragma unroll
-            for (int d = 0; d < 8; ++d) {
+                for (int dd = 0; dd < 8; ++dd) {
 #pragma unroll
-                for (int rq = 0; rq < 4; ++rq) {
-                    const int dim = 256 * kh + 32 * d + 8 * rq + 4 * half;
-                    const float v0 = acc[d][4 * rq + 0] * inv, v1 = acc[d][4 * rq + 1] * inv;
-                    const float v2 = acc[d][4 * rq + 2] * inv, v3 = acc[d][4 * rq + 3] * inv;
-                    if (final_out) {
-                        const int64_t o = ((int64_t)j * H + head) * kDv + dim;
-                        if (a.out_fp32) {
-                            *(f32x4*)((float*)a.out + o) = f32x4{v0, v1, v2, v3};
+                    for (int rq = 0; rq < 4; ++rq) {
+                        const int dim = 256 * kh + 32 * dd + 8 * rq + 4 * half;
+                        const float v0 = acc[dd][4 * rq + 0] * inv, v1 = acc[dd][4 * rq + 1] * inv;
+                        const float v2 = acc[dd][4 * rq + 2] * inv, v3 = acc[dd][4 * rq + 3] * inv;
+                        if (final_out) {
+                            const int64_t o = ((int64_t)j * H + head) * kDv + dim;
+                            if (a.out_fp32) {
+                                *(f32x4*)((float*)a.out + o) = f32x4{v0, v1, v2, v3};
+                            } else {
+                                const bf16x4 w = {(__bf16)v0, (__bf16)v1, (__bf16)v2, (__bf16)v3};
+                                *(bf16x4*)((__bf16*)a.out + o) = w;
+                            }
                         } else {
-                            const bf16x4 w = {(__bf16)v0, (__bf16)v1, (__bf16)v2, (__bf16)v3};
-                            *(bf16x4*)((__bf16*)a.out + o) = w;
+                            const int64_t o = ((int64_t)slot * H + head) * kDv + dim;
+                            *(f32x4*)(a.o_part + o) = f32x4{v0, v1, v2, v3};
                         }
-                    } else {
-                        const int64_t o = ((int64_t)slot * H + head) * kDv + dim;
-                        *(f32x4*)(a.o_part + o) = f32x4{v0, v1, v2, v3};
                     }
                 }
             }
-            if (kh == 0 && lane < 32) {
-                const float lse_v = l_run > 0.f ? (m_run + log2f(l_run)) * 0.69314718055994531f : -INFINITY;
+            if (kh == 0 && lane < 32 && head_ok) {
+                const float lse_v = l_run > 0.f ? (c * m_run + log2f(l_run)) * 0.69314718055994531f : -INFINITY;
                 if (final_out) a.lse[((int64_t)b * H + head) * a.s_q + iq] = lse_v;
                 else a.lse_part[(int64_t)slot * H + head] = lse_v;
             }

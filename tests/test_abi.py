@@ -52,7 +52,7 @@ def _problem(**kw):
 def test_plan_host_only():
     import mla_decode_amd as mla
     m = mla.plan(_problem(), num_cus=256)
-    assert m.num_head_blocks == 1 and m.num_partitions == 256 and m.fixed_overhead == 1
+    assert m.num_head_blocks == 1 and m.num_partitions == 256 and m.fixed_overhead == 0
     assert m.max_splits == 64 + 256
     assert m.bytes == (8 + 5 * 256 + 64 + 1) * 4
     assert mla.workspace_bytes(m) == 320 * 128 * 513 * 4
