@@ -165,6 +165,19 @@ mla_status_t mla_combine(int32_t num_items, int32_t h_q, int32_t s_q, const floa
                          const float *lse_part, const int32_t *split_offsets, int32_t out_dtype,
                          void *out, float *lse, void *stream);
 
+/* Test hook: the partial-attention kernel of mla_decode_fwd /
+ * mla_sparse_decode_fwd alone, without the LSE combine.  Items whose KV range
+ * lies in one partition get out and lse as usual; every other item leaves its
+ * normalised partials in ``workspace`` (layout as in mla_combine: o_part
+ * first, then lse_part at float offset max_splits*h_q*512) and its out/lse
+ * untouched.  ``table_or_indices`` is block_table (dense) or indices (sparse);
+ * cache_seqlens is ignored for sparse problems.  Same errors as
+ * mla_decode_fwd. */
+mla_status_t mla_debug_decode_partial(const mla_problem_t *problem, const void *q, const void *kv_cache,
+                                      const int32_t *table_or_indices, const int32_t *cache_seqlens,
+                                      const mla_metadata_t *meta, void *workspace, size_t workspace_bytes,
+                                      void *out, float *lse, void *stream);
+
 /* Test hook for the row resolution: writes, for every item j and KV slot t < tiles_j*64, the
  * physical cache row the decode kernels read for that slot, or -1 where the
  * slot is masked; rows_out is device int32 [batch*s_q, row_stride] with

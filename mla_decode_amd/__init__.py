@@ -134,6 +134,22 @@ def debug_gather_rows(problem, table_or_indices, cache_seqlens, rows_out, stream
         ctypes.byref(problem), _ptr(table_or_indices), _ptr(cache_seqlens), _ptr(rows_out), _stream(stream)))
 
 
+def debug_decode_partial(problem, q, kv_cache, table_or_indices, cache_seqlens, meta, workspace, out, lse,
+                         stream=None):
+    """Test hook: the partial-attention kernel alone (mla_debug_decode_partial)."""
+    lib = _lib.load()
+    _need(q, "q", torch.bfloat16)
+    _need(kv_cache, "kv_cache", None)
+    _need(table_or_indices, "table_or_indices", torch.int32)
+    _need(workspace, "workspace", None)
+    _need(out, "out", None)
+    _need(lse, "lse", torch.float32)
+    _lib.check("mla_debug_decode_partial", lib.mla_debug_decode_partial(
+        ctypes.byref(problem), _ptr(q), _ptr(kv_cache), _ptr(table_or_indices), _ptr(cache_seqlens),
+        ctypes.byref(meta), _ptr(workspace), workspace.numel() * workspace.element_size(), _ptr(out), _ptr(lse),
+        _stream(stream)))
+
+
 class Decoder:
     """Owns the per-shape plan, metadata buffer, workspace and outputs for one
     decode problem; ``step()`` runs the whole hot path (metadata + decode)."""
@@ -152,6 +168,12 @@ class Decoder:
 
     def metadata(self, cache_seqlens=None, stream=None):
         get_decode_metadata(self.problem, cache_seqlens, self.meta, self.meta_buf, stream)
+
+    def decode_partial(self, q, kv_cache, block_table=None, cache_seqlens=None, indices=None, stream=None):
+        """The partial-attention kernel alone (test and measurement hook)."""
+        toi = indices if self.problem.topk > 0 else block_table
+        debug_decode_partial(self.problem, q, kv_cache, toi, cache_seqlens, self.meta, self.workspace, self.out,
+                             self.lse, stream)
 
     def decode(self, q, kv_cache, block_table=None, cache_seqlens=None, indices=None, stream=None):
         if self.problem.topk > 0:

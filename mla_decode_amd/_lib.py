@@ -20,7 +20,7 @@ OUT_FP32 = 1
 
 EXPORTED = ("mla_abi_version", "mla_status_string", "mla_plan", "mla_workspace_bytes",
             "mla_get_decode_metadata", "mla_decode_fwd", "mla_sparse_decode_fwd", "mla_combine",
-            "mla_debug_gather_rows")
+            "mla_debug_gather_rows", "mla_debug_decode_partial")
 
 
 class Problem(ctypes.Structure):
@@ -73,6 +73,8 @@ def load():
     lib.mla_combine.argtypes = [i32, i32, i32, vp, vp, vp, i32, vp, vp, vp]
     lib.mla_debug_gather_rows.restype = ctypes.c_int
     lib.mla_debug_gather_rows.argtypes = [P(Problem), vp, vp, vp, vp]
+    lib.mla_debug_decode_partial.restype = ctypes.c_int
+    lib.mla_debug_decode_partial.argtypes = [P(Problem), vp, vp, vp, vp, P(Metadata), vp, ctypes.c_size_t, vp, vp, vp]
     _lib = lib
     return lib
 

@@ -86,7 +86,7 @@ mla_status_t check_meta(const mla_problem_t* p, const mla_metadata_t* m) {
 mla_status_t run_decode(const mla_problem_t* p, bool sparse, const void* q, const void* kv,
                         const int32_t* block_table, const int32_t* cache_seqlens, const int32_t* indices,
                         const mla_metadata_t* meta, void* ws, size_t ws_bytes, void* out, float* lse,
-                        void* stream) {
+                        void* stream, bool run_combine = true) {
     mla_status_t st = validate(p);
     if (st != MLA_OK) return st;
     if (sparse != (p->topk > 0)) return MLA_ERR_INVALID_ARG;
@@ -137,7 +137,7 @@ mla_status_t run_decode(const mla_problem_t* p, bool sparse, const void* q, cons
     c.s_q = p->s_q;
     c.out_fp32 = a.out_fp32;
     c.skip_single = 1;
-    if (mla::launch_combine(c, s) != hipSuccess) return MLA_ERR_HIP;
+    if (run_combine && mla::launch_combine(c, s) != hipSuccess) return MLA_ERR_HIP;
     return MLA_OK;
 }
 
@@ -239,6 +239,17 @@ mla_status_t mla_combine(int32_t num_items, int32_t h_q, int32_t s_q, const floa
     c.out_fp32 = out_dtype == MLA_OUT_FP32;
     c.skip_single = 0;
     return mla::launch_combine(c, (hipStream_t)stream) == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+}
+
+mla_status_t mla_debug_decode_partial(const mla_problem_t* problem, const void* q, const void* kv_cache,
+                                      const int32_t* table_or_indices, const int32_t* cache_seqlens,
+                                      const mla_metadata_t* meta, void* workspace, size_t workspace_bytes,
+                                      void* out, float* lse, void* stream) {
+    if (!problem) return MLA_ERR_INVALID_ARG;
+    const bool sparse = problem->topk > 0;
+    return run_decode(problem, sparse, q, kv_cache, sparse ? nullptr : table_or_indices,
+                      sparse ? nullptr : cache_seqlens, sparse ? table_or_indices : nullptr, meta, workspace,
+                      workspace_bytes, out, lse, stream, false);
 }
 
 mla_status_t mla_debug_gather_rows(const mla_problem_t* problem, const int32_t* table_or_indices,

@@ -226,6 +226,39 @@ def test_combine_standalone():
         assert np.all(np.abs(gl[fin] - rl[fin]) < 1e-5)
 
 
+def test_partial_hook_plus_combine_equals_decode():
+    """mla_debug_decode_partial followed by mla_combine over its workspace
+    gives exactly what mla_decode_fwd gives, for a shape where every item is
+    split (and for a sparse one)."""
+    import mla_decode_amd as mla
+    _say("partial hook")
+    for w in (make_dense(4, 1, 128, [4096, 4000, 3001, 2048], pool_blocks=300, seed=31, device=DEV),
+              make_sparse(3, 1, 128, pool_tokens_per_seq=8192, topk=2048, seed=32, device=DEV)):
+        dec = mla.Decoder.for_workload(w, DEV)
+        dec.metadata(None if w.topk else w.cache_seqlens)
+        out1, lse1 = dec.decode(w.q, w.kv, w.block_table, w.cache_seqlens, w.indices)
+        out1, lse1 = out1.clone(), lse1.clone()
+        dec.out.zero_()
+        dec.lse.zero_()
+        dec.decode_partial(w.q, w.kv, w.block_table, w.cache_seqlens, w.indices)
+        m = dec.meta
+        items = w.batch * w.s_q
+        slots = m.max_splits
+        ws = dec.workspace.view(torch.float32)
+        o_part = ws[:slots * w.h_q * 512]
+        lse_part = ws[slots * w.h_q * 512: slots * w.h_q * 513]
+        so_off = 8 + 5 * m.num_partitions
+        split_offsets = dec.meta_buf.view(torch.int32)[so_off: so_off + items + 1]
+        nsplit = (split_offsets[1:] - split_offsets[:-1]).cpu()
+        assert bool((nsplit > 1).all()), nsplit
+        out2 = torch.empty_like(out1)
+        lse2 = torch.empty_like(lse1)
+        mla.combine(items, w.h_q, w.s_q, o_part, lse_part, split_offsets, out2, lse2)
+        torch.cuda.synchronize()
+        assert torch.equal(out1.view(torch.int16), out2.view(torch.int16))
+        assert torch.equal(lse1, lse2)
+
+
 # ------------------------------------------------------------------ full-size workloads (sampled)
 
 def _sampled(w, items):

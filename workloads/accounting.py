@@ -8,7 +8,9 @@ cost-analysis page, "FlashMLA" cost model):
   plus q (576 bf16 per head), out (512 per head, 2 or 4 B), lse (4 B per
   head), and the block table or top-k indices (4 B each).
 Split partials and scheduler metadata are implementation overhead and are not
-counted here.
+counted here.  ``partial_bytes`` (KV rows, q, table or indices) is what the
+partial-attention kernel alone must move; the outputs of split items are
+written by the combine.
 """
 
 import math
@@ -51,7 +53,7 @@ def flops_and_bytes(w):
     out_bytes = B * S * H * D_V * out_elem + B * S * H * 4
     total = kv_bytes + q_bytes + out_bytes + side
     return {'flops': flops, 'bytes': float(total), 'kv_bytes': float(kv_bytes),
-            'pairs': pairs, 'kv_rows': kv_rows}
+            'partial_bytes': float(kv_bytes + q_bytes + side), 'pairs': pairs, 'kv_rows': kv_rows}
 
 
 def cost_model_flashmla(b, h, s, t, k=512, p=64, w=2):
