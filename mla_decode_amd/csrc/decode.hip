@@ -94,7 +94,7 @@ __device__ __forceinline__ i32x4 buffer_rsrc(const void* base, int stride, int n
 // LDS at M0).  They are issued through inline assembly so that the compiler
 // does not treat them as pending LDS stores: it would otherwise wait for every
 // in-flight tile load before the next LDS read of any other tile.  The kernel
-// orders them itself: s_waitcnt vmcnt(0) by every wave, then a workgroup
+// orders them itself: s_waitcnt vmcnt(0) by each wave that issued copies, then a workgroup
 // barrier, before a filled tile is read.
 // The immediate offset moves both the global source and the LDS destination
 // (LDS address = M0 + offset + 16 * lane), so M0 is set to the destination
@@ -612,7 +612,7 @@ __global__ void __launch_bounds__(kThreads, 1) decode_kernel(const DecodeArgs a)
         auto step_odd_end = [&](int t) __attribute__((always_inline)) {
             if (t + 1 < ns) {
                 if (FP8) fp8_store(sm.tile[0] + opaque_tile_offset((t + 1) % kNBuf), f8, f8_tok, f8_p);
-                else __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's tile copies
+                else if (grp == 1) __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): group 1's tile copies
             }
             if (!SPARSE) {
                 if (((g0 + t + 3) >> 1) - pt_base >= 64) load_pages((g0 + t) >> 1);
