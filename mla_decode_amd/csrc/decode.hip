@@ -69,6 +69,15 @@ __device__ __forceinline__ int opaque_tile_offset(int idx) {
     return off;
 }
 
+// Lane id recomputed where it is used (bit count of an all-ones mask below
+// this lane).  The mask goes through an empty asm statement so that the
+// compiler cannot hoist the result out of a loop and hold (or spill) it.
+__device__ __forceinline__ int lane_id() {
+    unsigned m = ~0u;
+    __asm__ volatile("" : "+s"(m));
+    return (int)__builtin_amdgcn_mbcnt_hi(m, __builtin_amdgcn_mbcnt_lo(m, 0u));
+}
+
 __device__ __forceinline__ bf16x8 pack8(const float* v) {
     bf16x8 r;
 #pragma unroll
@@ -339,35 +348,7 @@ __global__ void __launch_bounds__(kThreads, 1) decode_kernel(const DecodeArgs a)
         const int gend = min(2 * t1, (nslots + kSubTok - 1) / kSubTok);
         const int ns = gend - g0;
 
-        // ---- Q: latent dims 256*kh.. in registers, RoPE part to LDS ----
-        bf16x8 qf[16];
-        {
-            const bf16x8* qp = (const bf16x8*)((const unsigned char*)a.q +
-                                               ((int64_t)j * H + (head_ok ? head : 0)) * kRowBytes);
-#pragma unroll
-            for (int kk = 0; kk < 16; ++kk) {
-                bf16x8 v = qp[32 * kh + 2 * kk + half];
-                if (!head_ok) v = bf16x8{};
-                qf[kk] = v;
-            }
-#pragma unroll
-            for (int e = 0; e < 2; ++e) {
-                const int idx = tid + kThreads * e;          // 0..1023 = [hb2][kr][lane]
-                const int ln = idx & 63, kr = (idx >> 6) & 3, hb2 = idx >> 8;
-                const int hq = hblk * kHeadsPerWG + hb2 * 32 + (ln & 31);
-                bf16x8 v = {};
-                if (hq < H)
-                    v = ((const bf16x8*)((const unsigned char*)a.q + ((int64_t)j * H + hq) * kRowBytes))[64 + 2 * kr + (ln >> 5)];
-                sm.qr[hb2][kr][ln] = v;
-            }
-        }
-
-        f32x16 acc[8];
-#pragma unroll
-        for (int d = 0; d < 8; ++d) acc[d] = f32x16{};
-        float m_run = -INFINITY, l_run = 0.f;
-
-        // dense: page ids of tiles it, it+1, it+2 (one 64-token page = two tiles)
+        // ---- prologue: page ids, Q and tile 0 are requested together ----
         // dense: page ids of 64 consecutive pages of item j, one per lane, read
         // with v_readlane.  A scalar load here would be waited for with
         // lgkmcnt(0), which also drains every outstanding LDS operation.
@@ -383,6 +364,40 @@ __global__ void __launch_bounds__(kThreads, 1) decode_kernel(const DecodeArgs a)
         auto page_of = [&](int g) __attribute__((always_inline)) {
             return __builtin_amdgcn_readlane(pt_v, (g >> 1) - pt_base);
         };
+
+        // Q: latent dims 256*kh.. in registers, RoPE part to LDS.  The lane
+        // terms of the addresses are rebuilt from the lane id (mbcnt), so that
+        // they are not kept (or spilled) across the item loop.
+        bf16x8 qf[16], qrv[2];
+        {
+            const int tid_o = wave * 64 + lane_id();
+            const int head_o = hblk * kHeadsPerWG + hb * 32 + (tid_o & 31);
+            const int half_o = (tid_o >> 5) & 1;
+            const bf16x8* qp = (const bf16x8*)((const unsigned char*)a.q +
+                                               ((int64_t)j * H + (head_o < H ? head_o : 0)) * kRowBytes);
+#pragma unroll
+            for (int kk = 0; kk < 16; ++kk) {
+                bf16x8 v = qp[32 * kh + 2 * kk + half_o];
+                if (!head_ok) v = bf16x8{};
+                qf[kk] = v;
+            }
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+                const int idx = tid_o + kThreads * e;        // 0..1023 = [hb2][kr][lane]
+                const int ln = idx & 63, kr = (idx >> 6) & 3, hb2 = idx >> 8;
+                const int hq = hblk * kHeadsPerWG + hb2 * 32 + (ln & 31);
+                bf16x8 v = {};
+                if (hq < H)
+                    v = ((const bf16x8*)((const unsigned char*)a.q + ((int64_t)j * H + hq) * kRowBytes))[64 + 2 * kr + (ln >> 5)];
+                qrv[e] = v;
+            }
+        }
+
+        f32x16 acc[8];
+#pragma unroll
+        for (int d = 0; d < 8; ++d) acc[d] = f32x16{};
+        float m_run = -INFINITY, l_run = 0.f;
+
         int pg0 = 0, pg1 = 0, pg2 = 0;
         if (!SPARSE) {
             pg0 = page_of(g0);
@@ -394,13 +409,17 @@ __global__ void __launch_bounds__(kThreads, 1) decode_kernel(const DecodeArgs a)
             for (int u = 0; u < 2; ++u)
                 if (u < ns) sm.rows[u][lane] = (int)rr.row(j, (g0 + u) * kSubTok + lane, nslots);
         }
-        lds_barrier();
+        if (SPARSE || FP8) lds_barrier();   // row ids of tiles 0 and 1 for every wave
 
         auto issue_fill = [&](int it, int page) __attribute__((always_inline)) {
             const int g = g0 + it;
             const int dst = (int)(size_t)(lds_void_t*)&sm.tile[0][0] + opaque_tile_offset(it % kNBuf);
             if (SPARSE) fill_sparse(dst, srs, sm.rows[it & 3][ftok], fcol, wave);
-            else fill_dense(dst, kv, page, g & 1, nslots - g * kSubTok, a.num_rows, fbase, wave);
+            else {
+                const int ln = lane_id();
+                const int fb = ((ln & 31) ^ (4 * (ln >> 5) + 8 * (wave & 1))) * kRowBytes + 16 * (ln >> 5);
+                fill_dense(dst, kv, page, g & 1, nslots - g * kSubTok, a.num_rows, fb, wave);
+            }
         };
         Fp8Regs f8;
         auto fp8_row = [&](int it, int page) __attribute__((always_inline)) -> int64_t {
@@ -414,8 +433,13 @@ __global__ void __launch_bounds__(kThreads, 1) decode_kernel(const DecodeArgs a)
             fp8_store(sm.tile[0], f8, f8_tok, f8_p);
         } else {
             issue_fill(0, pg0);
-            __builtin_amdgcn_s_waitcnt(0x0F70);
         }
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+            const int idx = tid + kThreads * e;
+            sm.qr[idx >> 8][(idx >> 6) & 3][idx & 63] = qrv[e];
+        }
+        if (!FP8) __builtin_amdgcn_s_waitcnt(0x0F70);
         lds_barrier();
 
         // ---- step pipeline ----
