@@ -310,7 +310,9 @@ __global__ void __launch_bounds__(kThreads, 1) decode_kernel(const DecodeArgs a)
     const bool head_ok = head < H;
 
     const i32x4 srs = buffer_rsrc(kv, kRowBytes, (int)a.num_rows);
-    const int f8_tok = tid >> 4, f8_p = tid & 15;    // FP8 fill role
+    // FP8 fill role: thread (token tid/16, part tid%16), rebuilt from the lane id where used
+    auto f8_tok = [&]() __attribute__((always_inline)) { return wave * 4 + (lane_id() >> 4); };
+    auto f8_p = [&]() __attribute__((always_inline)) { return lane_id() & 15; };
     const int nload = fill_loads(wave);
     const int ftok = l32 ^ (4 * half + 8 * (wave & 1));   // bf16 fill: token this lane copies
     const int fbase = ftok * kRowBytes + 16 * half;       // dense fill source offset (+32k)
@@ -359,6 +361,8 @@ __global__ void __launch_bounds__(kThreads, 1) decode_kernel(const DecodeArgs a)
             pt_base = first;
             const int pi = first + lane;
             pt_v = pi < npages_item ? a.block_table[(int64_t)b_item * a.max_blocks + pi] : 0;
+            // waited for here, so that no later read of pt_v waits for other loads
+            __builtin_amdgcn_s_waitcnt(0x0F70);
         };
         if (!SPARSE) load_pages(g0 >> 1);
         auto page_of = [&](int g) __attribute__((always_inline)) {
@@ -424,13 +428,13 @@ __global__ void __launch_bounds__(kThreads, 1) decode_kernel(const DecodeArgs a)
         Fp8Regs f8;
         auto fp8_row = [&](int it, int page) __attribute__((always_inline)) -> int64_t {
             const int g = g0 + it;
-            if (SPARSE) return sm.rows[it & 3][f8_tok];
-            return row_in_page(page, (g & 1) * kSubTok + f8_tok, nslots - (g & ~1) * kSubTok, a.num_rows);
+            if (SPARSE) return sm.rows[it & 3][f8_tok()];
+            return row_in_page(page, (g & 1) * kSubTok + f8_tok(), nslots - (g & ~1) * kSubTok, a.num_rows);
         };
         // tile 0 lands before step 0
         if (FP8) {
-            fp8_load(f8, kv, fp8_row(0, pg0), f8_p);
-            fp8_store(sm.tile[0], f8, f8_tok, f8_p);
+            fp8_load(f8, kv, fp8_row(0, pg0), f8_p());
+            fp8_store(sm.tile[0], f8, f8_tok(), f8_p());
         } else {
             issue_fill(0, pg0);
         }
@@ -625,7 +629,7 @@ __global__ void __launch_bounds__(kThreads, 1) decode_kernel(const DecodeArgs a)
             int next_row = -1;
             if (SPARSE && wave == 0 && lane < kSubTok && t + 2 < ns)
                 next_row = (int)rr.row(j, (g0 + t + 2) * kSubTok + lane, nslots);
-            if (FP8 && t + 1 < ns) fp8_load(f8, kv, fp8_row(t + 1, pg1), f8_p);
+            if (FP8 && t + 1 < ns) fp8_load(f8, kv, fp8_row(t + 1, pg1), f8_p());
             return next_row;
         };
         auto step_even_end = [&](int t, int next_row) __attribute__((always_inline)) {
@@ -635,7 +639,7 @@ __global__ void __launch_bounds__(kThreads, 1) decode_kernel(const DecodeArgs a)
         // end of step 2t+1: tile t+1 has landed
         auto step_odd_end = [&](int t) __attribute__((always_inline)) {
             if (t + 1 < ns) {
-                if (FP8) fp8_store(sm.tile[0] + opaque_tile_offset((t + 1) % kNBuf), f8, f8_tok, f8_p);
+                if (FP8) fp8_store(sm.tile[0] + opaque_tile_offset((t + 1) % kNBuf), f8, f8_tok(), f8_p());
                 else if (grp == 1) __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): group 1's tile copies
             }
             if (!SPARSE) {
