@@ -3,7 +3,8 @@
 // Combine: one workgroup per (item, 4 heads); 64 lanes x 8 dims cover the 512
 // output dims of a head.  With m* = max_k lse_k and w_k = exp(lse_k - m*):
 // out = sum_k w_k o_k / sum_k w_k and lse = m* + ln sum_k w_k, which is the
-// pairwise split merge applied to all partials at once.
+// pairwise split merge applied to all partials at once (computed a chunk of
+// splits at a time with a running maximum).
 
 #include "common.h"
 #include "kernels.h"
@@ -19,25 +20,53 @@ __global__ void __launch_bounds__(256) combine_kernel(const CombineArgs a) {
     const int n = s1 - s0;
     if (a.skip_single && n == 1) return;
     const int H = a.h_q;
-    float m = -INFINITY;
-    for (int k = s0; k < s1; ++k) m = fmaxf(m, a.lse_part[(int64_t)k * H + h]);
+    // Splits are merged kSplitChunk at a time, every load of a chunk issued
+    // before any is used; across chunks the merge is online (running max m).
+    constexpr int kSplitChunk = 4;
+    float m = -INFINITY, wsum = 0.f;
     float o[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    for (int k0 = s0; k0 < s1; k0 += kSplitChunk) {
+        float lk[kSplitChunk];
+        f32x4 u[kSplitChunk], v[kSplitChunk];
+#pragma unroll
+        for (int c = 0; c < kSplitChunk; ++c) {
+            const int k = k0 + c;
+            lk[c] = -INFINITY;
+            u[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+            v[c] = u[c];
+            if (k < s1) {
+                lk[c] = a.lse_part[(int64_t)k * H + h];
+                const f32x4* src = (const f32x4*)(a.o_part + ((int64_t)k * H + h) * kDv + lane * 8);
+                u[c] = src[0];
+                v[c] = src[1];
+            }
+        }
+        float mc = m;
+#pragma unroll
+        for (int c = 0; c < kSplitChunk; ++c) mc = fmaxf(mc, lk[c]);
+        if (mc == -INFINITY) continue;                       // nothing finite yet
+        const float sc = m == -INFINITY ? 0.f : __expf(m - mc);
+        wsum *= sc;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o[e] *= sc;
+#pragma unroll
+        for (int c = 0; c < kSplitChunk; ++c) {
+            const float w = lk[c] == -INFINITY ? 0.f : __expf(lk[c] - mc);
+            wsum += w;
+            o[0] += w * u[c][0]; o[1] += w * u[c][1]; o[2] += w * u[c][2]; o[3] += w * u[c][3];
+            o[4] += w * v[c][0]; o[5] += w * v[c][1]; o[6] += w * v[c][2]; o[7] += w * v[c][3];
+        }
+        m = mc;
+    }
     float lse_v = -INFINITY;
     if (n > 0 && m != -INFINITY) {
-        float wsum = 0.f;
-        for (int k = s0; k < s1; ++k) {
-            const float lk = a.lse_part[(int64_t)k * H + h];
-            const float w = lk == -INFINITY ? 0.f : __expf(lk - m);
-            wsum += w;
-            const f32x4* src = (const f32x4*)(a.o_part + ((int64_t)k * H + h) * kDv + lane * 8);
-            const f32x4 u = src[0], v = src[1];
-            o[0] += w * u[0]; o[1] += w * u[1]; o[2] += w * u[2]; o[3] += w * u[3];
-            o[4] += w * v[0]; o[5] += w * v[1]; o[6] += w * v[2]; o[7] += w * v[3];
-        }
         const float inv = 1.f / wsum;
 #pragma unroll
         for (int e = 0; e < 8; ++e) o[e] *= inv;
         lse_v = m + __logf(wsum);
+    } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o[e] = 0.f;
     }
     const int64_t off = ((int64_t)item * H + h) * kDv + lane * 8;
     if (a.out_fp32) {

@@ -202,14 +202,20 @@ def test_combine_standalone():
     import mla_decode_amd as mla
     _say("combine")
     g = torch.Generator().manual_seed(2)
-    H, S_, B = 8, 2, 3
-    ns = [0, 1, 3, 2, 4, 1]
+    H, S_, B = 8, 2, 5
+    # split counts include items with more splits than the kernel merges per
+    # chunk (4), so that the running-maximum merge across chunks is exercised
+    ns = [0, 1, 3, 2, 4, 1, 7, 9, 5, 12]
     so = np.concatenate([[0], np.cumsum(ns)]).astype(np.int32)
     T = int(so[-1])
     o = torch.randn(T, H, 512, generator=g)
     lse = torch.randn(T, H, generator=g) * 3
-    lse[2, 1] = -float("inf")
-    lse[7, :] = -float("inf")            # an item (5) whose only split is empty
+    lse[2, 1] = -float("inf")            # one empty split of item 2, one head
+    lse[7, :] = -float("inf")            # one empty split of item 4
+    lse[10, :] = -float("inf")           # item 5: its only split is empty
+    lse[11:15, :] = -float("inf")        # item 6: the whole first chunk is empty
+    lse[22:26, :] = -float("inf")        # item 7: the whole second chunk is empty
+    lse[41, :] += 40.0                   # item 9: the maximum sits in its third chunk
     out = torch.empty(B, S_, H, 512, dtype=torch.float32, device=DEV)
     lo = torch.empty(B, H, S_, dtype=torch.float32, device=DEV)
     mla.combine(B * S_, H, S_, o.to(DEV), lse.to(DEV), torch.from_numpy(so).to(DEV), out, lo)
