@@ -562,6 +562,10 @@ __global__ void __launch_bounds__(kThreads, 1) decode_kernel(const DecodeArgs a)
             // ``on`` is a compile-time constant here, so the pieces are straight-line code
             FillCtx fc = fc_in;
             fc.on = decltype(fill_c)::value != 0 && !FP8;
+            // The softmax wave is issue-bound on VALU while the other wave of
+            // the SIMD needs one issue slot per MFMA: give the softmax wave the
+            // higher issue priority for the duration of the step.
+            __builtin_amdgcn_s_setprio(2);
             const int g = g0 + t;
             const int tv = nslots - g * kSubTok;
             const int pg_t = SPARSE ? 0 : page_of(g);
@@ -623,6 +627,7 @@ __global__ void __launch_bounds__(kThreads, 1) decode_kernel(const DecodeArgs a)
 #pragma unroll
             for (int e = 0; e < 8; ++e) { p0[e] = (__bf16)s[e]; p1[e] = (__bf16)s[8 + e]; }
             fill_piece(fc, IntC<8>{});
+            __builtin_amdgcn_s_setprio(0);
         };
         // step 2t: FP8 tile t+1 to registers; sparse row ids of tile t+2
         auto step_even_begin = [&](int t) __attribute__((always_inline)) -> int {
