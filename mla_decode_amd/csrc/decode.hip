@@ -124,7 +124,6 @@ __device__ __forceinline__ void dma_struct_x4(const i32x4& rs, int row, int voff
 // pieces w, w+8, w+16, w+24 and, for w < 4, 32+w.  All pieces of a wave have
 // k & 1 = w & 1, so lane l always reads token ft = (l & 31) ^ (4 half + 8 (w & 1))
 // and column 2k + half: source offset ft*1152 + 16 half + 32k.
-__device__ __forceinline__ int fill_loads(int wave) { return wave < 4 ? 5 : 4; }
 
 // dense: the tile is one half of a 64-token page; tokens >= tok_valid are masked
 // ``dst`` is the LDS byte address of the tile buffer.
@@ -208,18 +207,12 @@ __device__ __forceinline__ void lds_barrier() {
     __asm__ volatile("" ::: "memory");
 }
 
-// s_waitcnt vmcnt(n) for a wave-uniform n in {0, 4, 5}
-__device__ __forceinline__ void wait_vm(int n) {
-    if (n >= 5) __builtin_amdgcn_s_waitcnt(0x0F75);
-    else if (n == 4) __builtin_amdgcn_s_waitcnt(0x0F74);
-    else __builtin_amdgcn_s_waitcnt(0x0F70);
-}
-
 // Instruction order of the MFMA step, pinned for the scheduler: the LDS
-// reads of operations I0 and I0+1 first, then each MFMA followed by the reads
-// of the operation two ahead (two for a PV step or a RoPE step, one for a
-// latent QK step), then the four stores of the partial scores.
-constexpr int kSchedValu = 0x002, kSchedMfma = 0x008, kSchedDsRead = 0x100, kSchedDsWrite = 0x200;
+// reads of the first kMstepLookahead operations, then each MFMA followed by
+// the reads of the operation kMstepLookahead ahead (two for a PV step or a
+// RoPE step, one for a latent QK step), then the four stores of the partial
+// scores.
+constexpr int kSchedMfma = 0x008, kSchedDsRead = 0x100, kSchedDsWrite = 0x200;
 constexpr int kMstepLookahead = 3;   // operations whose operands are in flight
 constexpr int mstep_reads(int i) { return (i < 16 || i >= 32) ? 2 : 1; }
 
@@ -313,7 +306,6 @@ __global__ void __launch_bounds__(kThreads, 1) decode_kernel(const DecodeArgs a)
     // FP8 fill role: thread (token tid/16, part tid%16), rebuilt from the lane id where used
     auto f8_tok = [&]() __attribute__((always_inline)) { return wave * 4 + (lane_id() >> 4); };
     auto f8_p = [&]() __attribute__((always_inline)) { return lane_id() & 15; };
-    const int nload = fill_loads(wave);
     const int ftok = l32 ^ (4 * half + 8 * (wave & 1));   // bf16 fill: token this lane copies
     const int fbase = ftok * kRowBytes + 16 * half;       // dense fill source offset (+32k)
     const int fcol = 16 * half;                            // sparse fill column offset (+32k)
