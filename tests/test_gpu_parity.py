@@ -152,6 +152,23 @@ def test_split_count_invariance():
         assert np.max(np.abs(o - outs[0])) <= 1e-2
 
 
+@pytest.mark.parametrize("kv_format", ["bf16", "fp8"])
+def test_long_partition_crosses_page_window(kv_format):
+    """A partition that walks more than 64 pages reloads its window of page
+    ids on the way (the kernel holds 64 page ids at a time); with two CUs the
+    partitions also start mid-item and span item boundaries."""
+    _say(f"long partition {kv_format}")
+    make = make_dense if kv_format == "bf16" else make_fp8_dense
+    w = make(3, 1, 32, [64 * 150 + 17, 64 * 70, 300], seed=12, device=DEV)
+    ro, rl = oracle(w)
+    for num_cus in (1, 2):
+        go, gl, _ = run_library(w, num_cus=num_cus)
+        if kv_format == "bf16":
+            _say(compare(go, gl, ro, rl))
+        else:
+            _say(compare(go, gl, ro, rl, rel_l2=FP8_REL_L2, max_abs=5e-2))
+
+
 def test_block_table_reshuffle_is_bitwise_invariant():
     _say("reshuffle")
     w = make_dense(2, 1, 128, [300, 190], seed=5, device=DEV, max_blocks=5, pool_blocks=12)
