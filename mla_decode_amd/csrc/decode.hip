@@ -52,6 +52,7 @@ struct __attribute__((aligned(16))) Smem {
     f32x4 xs[4][2][4][64];                  // partial S^T [head block][dim half][register quad][lane]
     bf16x8 qr[4][4][64];                    // RoPE part of Q as B fragments [head block][k-step][lane]
     int rows[4][kSubTok];                   // sparse: row ids of upcoming tiles (ring of 4)
+    float f8scale[8][64];                   // FP8: per-wave scales of the tile being converted (lanes 32.. pad)
     unsigned char tile[kNBuf][kSubBytes];   // 32-token KV tiles (bf16, swizzled)
 };
 
@@ -152,48 +153,53 @@ __device__ __forceinline__ void fill_sparse(int dst, const i32x4& rs, int row, i
     if (wave < 4) dma_struct_x4<0>(rs, row, fcol + 32 * (32 + wave), l0 + 32 * 1024);
 }
 
-// ---- FP8 tile fill: thread (token t = tid/16, part p = tid%16) owns latent
-// dims 32p..32p+31 (one scale tile) and, for p < 8, RoPE chunk p.
-struct Fp8Regs {
-    i32x4 codes[2];
-    float scale;
-    i32x4 rope;
-};
-
-__device__ __forceinline__ void fp8_load(Fp8Regs& r, const unsigned char* kv, int64_t row, int p) {
-    const i32x4 z = {0, 0, 0, 0};
-    r.codes[0] = z;
-    r.codes[1] = z;
-    r.scale = 0.f;
-    r.rope = z;
-    if (row >= 0) {
-        const unsigned char* base = kv + row * kFp8RowBytes;
-        r.codes[0] = *(const i32x4*)(base + 32 * p);
-        r.codes[1] = *(const i32x4*)(base + 32 * p + 16);
-        r.scale = *(const float*)(base + 512 + 4 * (p >> 2));
-        if (p < 8) r.rope = *(const i32x4*)(base + 528 + 16 * p);
-    }
+// ---- FP8 tile fill: the raw 656-B records are copied into the tile buffer
+// and dequantised there.  The 32 code bytes of part p (latent dims
+// 32p..32p+31) of every token land in LDS columns 4p+2 and 4p+3, two of the
+// four chunks their bf16 values end in; the RoPE bytes (already bf16) land in
+// columns 64..71, their final place; the scale of dims 128s.. lands in a
+// per-wave array.  Wave w copies and converts parts 2w and 2w+1 of all 32
+// tokens, so every raw byte is read by the lane that copied it, after that
+// wave's own vmcnt wait, and overwritten only by that lane.
+template <int IMM>
+__device__ __forceinline__ void dma_raw_x1(const i32x4& rs, int voff, int lds) {
+    __asm__ volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, 0 offen offset:%3 lds"
+                     :: "s"(lds - IMM), "v"(voff), "s"(rs), "i"(IMM) : "memory", "m0");
+}
+__device__ __forceinline__ void dma_struct_x1(const i32x4& rs, int row, int voff, int lds) {
+    const i32x2 va = {row, voff};
+    __asm__ volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, 0 idxen offen lds"
+                     :: "s"(lds), "v"(va), "s"(rs) : "memory", "m0");
 }
 
-// e4m3fn -> fp32 (exact), x scale in fp32, -> bf16 (round to nearest even)
-__device__ __forceinline__ void fp8_store(unsigned char* dst, const Fp8Regs& r, int t, int p) {
+// LDS token slot of lane l in a copy of columns (c, c+1): column c + (l >> 5),
+// slot l & 31, token = slot ^ col_xor(column)
+__device__ __forceinline__ int fp8_code_token(int l) { return (l & 31) ^ (8 + 4 * (l >> 5)); }   // c = 4p+2
+__device__ __forceinline__ int fp8_rope_token(int l, int w) { return (l & 31) ^ (4 * (l >> 5) + 8 * (w & 1)); }
+
+// e4m3fn -> fp32 (exact), x scale in fp32, -> bf16 (round to nearest even), in
+// place: lane l of wave w converts part 2w + (l >> 5) of token l & 31.
+__device__ __forceinline__ void fp8_convert(unsigned char* dst, const float* scales, int w, int l) {
+    const int t = l & 31, p = 2 * w + (l >> 5);
+    const i32x4 raw[2] = {*(const i32x4*)(dst + lds_chunk(t, 4 * p + 2) * 16),
+                          *(const i32x4*)(dst + lds_chunk(t, 4 * p + 3) * 16)};
+    const float sc = scales[t];
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
         float v[16];
 #pragma unroll
-        for (int w = 0; w < 4; ++w) {
-            const int word = r.codes[h][w];
+        for (int q = 0; q < 4; ++q) {
+            const int word = raw[h][q];
             auto lo = __builtin_amdgcn_cvt_pk_f32_fp8(word, false);
             auto hi = __builtin_amdgcn_cvt_pk_f32_fp8(word, true);
-            v[4 * w + 0] = lo[0] * r.scale;
-            v[4 * w + 1] = lo[1] * r.scale;
-            v[4 * w + 2] = hi[0] * r.scale;
-            v[4 * w + 3] = hi[1] * r.scale;
+            v[4 * q + 0] = lo[0] * sc;
+            v[4 * q + 1] = lo[1] * sc;
+            v[4 * q + 2] = hi[0] * sc;
+            v[4 * q + 3] = hi[1] * sc;
         }
         *(bf16x8*)(dst + lds_chunk(t, 4 * p + 2 * h) * 16) = pack8(v);
         *(bf16x8*)(dst + lds_chunk(t, 4 * p + 2 * h + 1) * 16) = pack8(v + 8);
     }
-    if (p < 8) *(i32x4*)(dst + lds_chunk(t, 64 + p) * 16) = r.rope;
 }
 
 // Workgroup barrier for LDS traffic only.  __syncthreads() also orders global
@@ -303,9 +309,7 @@ __global__ void __launch_bounds__(kThreads, 1) decode_kernel(const DecodeArgs a)
     const bool head_ok = head < H;
 
     const i32x4 srs = buffer_rsrc(kv, kRowBytes, (int)a.num_rows);
-    // FP8 fill role: thread (token tid/16, part tid%16), rebuilt from the lane id where used
-    auto f8_tok = [&]() __attribute__((always_inline)) { return wave * 4 + (lane_id() >> 4); };
-    auto f8_p = [&]() __attribute__((always_inline)) { return lane_id() & 15; };
+    const i32x4 srs8 = buffer_rsrc(kv, kFp8RowBytes, (int)a.num_rows);   // FP8 sparse: one record per row
     const int ftok = l32 ^ (4 * half + 8 * (wave & 1));   // bf16 fill: token this lane copies
     const int fbase = ftok * kRowBytes + 16 * half;       // dense fill source offset (+32k)
     const int fcol = 16 * half;                            // sparse fill column offset (+32k)
@@ -417,16 +421,49 @@ __global__ void __launch_bounds__(kThreads, 1) decode_kernel(const DecodeArgs a)
                 fill_dense(dst, kv, page, g & 1, nslots - g * kSubTok, a.num_rows, fb, wave);
             }
         };
-        Fp8Regs f8;
-        auto fp8_row = [&](int it, int page) __attribute__((always_inline)) -> int64_t {
+        // FP8: copy the raw records of tile it (page ``page``) into its buffer.
+        // With it >= ns the copies run on an empty range and write zeros into
+        // that buffer, which no step reads any more.
+        auto fp8_copy = [&](int it, int page) __attribute__((always_inline)) {
             const int g = g0 + it;
-            if (SPARSE) return sm.rows[it & 3][f8_tok()];
-            return row_in_page(page, (g & 1) * kSubTok + f8_tok(), nslots - (g & ~1) * kSubTok, a.num_rows);
+            const int l = lane_id();
+            const int dst = (int)(size_t)(lds_void_t*)&sm.tile[0][0] + opaque_tile_offset(it % kNBuf);
+            const int sdst = (int)(size_t)(lds_void_t*)&sm.f8scale[wave][0];
+            const int tc = fp8_code_token(l), tr = fp8_rope_token(l, wave);
+            const int wr = wave & 3;                       // waves w and w+4 copy the same RoPE columns
+            const int code_off = 64 * wave + 16 * (l >> 5);
+            const int rope_off = 528 + 16 * (2 * wr + (l >> 5));
+            const int scale_off = 512 + 4 * (wave >> 1);
+            const int code_lds = dst + (8 * wave + 2) * 512, rope_lds = dst + (64 + 2 * wr) * 512;
+            if (SPARSE) {
+                const bool live = it < ns;
+                const int rc = live ? sm.rows[it & 3][tc] : -1;
+                const int rr_ = live ? sm.rows[it & 3][tr] : -1;
+                const int rs_ = (live && l < kSubTok) ? sm.rows[it & 3][l] : -1;
+                dma_struct_x4<0>(srs8, rc, code_off, code_lds);
+                dma_struct_x4<32>(srs8, rc, code_off, code_lds + 2048);
+                dma_struct_x4<0>(srs8, rr_, rope_off, rope_lds);
+                dma_struct_x1(srs8, rs_, scale_off, sdst);
+            } else {
+                const bool ok = it < ns && page_ok(page, a.num_rows);
+                int nvalid = min(nslots - g * kSubTok, kSubTok);
+                if (!ok || nvalid < 0) nvalid = 0;
+                const i32x4 rs = buffer_rsrc(kv + (ok ? ((int64_t)page * kBlock + (g & 1) * kSubTok) * kFp8RowBytes : 0),
+                                             0, nvalid * kFp8RowBytes);
+                dma_raw_x4<0>(rs, tc * kFp8RowBytes + code_off, code_lds);
+                dma_raw_x4<32>(rs, tc * kFp8RowBytes + code_off, code_lds + 2048);
+                dma_raw_x4<0>(rs, tr * kFp8RowBytes + rope_off, rope_lds);
+                dma_raw_x1<0>(rs, l < kSubTok ? l * kFp8RowBytes + scale_off : 0x40000000, sdst);
+            }
+        };
+        auto fp8_dequant = [&](int it) __attribute__((always_inline)) {
+            fp8_convert(sm.tile[0] + opaque_tile_offset(it % kNBuf), sm.f8scale[wave], wave, lane_id());
         };
         // tile 0 lands before step 0
         if (FP8) {
-            fp8_load(f8, kv, fp8_row(0, pg0), f8_p());
-            fp8_store(sm.tile[0], f8, f8_tok(), f8_p());
+            fp8_copy(0, pg0);
+            __builtin_amdgcn_s_waitcnt(0x0F70);
+            fp8_dequant(0);
         } else {
             issue_fill(0, pg0);
         }
@@ -626,7 +663,7 @@ __global__ void __launch_bounds__(kThreads, 1) decode_kernel(const DecodeArgs a)
             int next_row = -1;
             if (SPARSE && wave == 0 && lane < kSubTok && t + 2 < ns)
                 next_row = (int)rr.row(j, (g0 + t + 2) * kSubTok + lane, nslots);
-            if (FP8 && t + 1 < ns) fp8_load(f8, kv, fp8_row(t + 1, pg1), f8_p());
+            if (FP8) fp8_copy(t + 1, pg1);
             return next_row;
         };
         auto step_even_end = [&](int t, int next_row) __attribute__((always_inline)) {
@@ -636,7 +673,10 @@ __global__ void __launch_bounds__(kThreads, 1) decode_kernel(const DecodeArgs a)
         // end of step 2t+1: tile t+1 has landed
         auto step_odd_end = [&](int t) __attribute__((always_inline)) {
             if (t + 1 < ns) {
-                if (FP8) fp8_store(sm.tile[0] + opaque_tile_offset((t + 1) % kNBuf), f8, f8_tok(), f8_p());
+                if (FP8) {
+                    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's copies of tile t+1
+                    fp8_dequant(t + 1);
+                }
                 else if (grp == 1) __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): group 1's tile copies
             }
             if (!SPARSE) {
