@@ -39,7 +39,7 @@
 extern "C" {
 #endif
 
-#define MLA_DECODE_ABI_VERSION 1
+#define MLA_DECODE_ABI_VERSION 2
 
 typedef enum {
     MLA_OK = 0,
@@ -84,6 +84,16 @@ typedef struct {
     int32_t kv_format;           /* mla_kv_format_t */
     int32_t out_dtype;           /* mla_out_dtype_t */
     float softmax_scale;         /* > 0; multiplies q . k before the softmax */
+    /* Online-softmax running max (the flash-attention sparse-MLA note on the
+     * exact running max, "threshold branch" and "measurements").  0: exact
+     * running max, raised whenever a tile holds a larger score.  tau in
+     * (0, 30]: lazy rescale, the running max of a row is raised only when a
+     * tile's max exceeds it by more than tau, in log2 units of the scaled
+     * scores, so probabilities reach up to 2^tau and the output rescale runs
+     * rarely.  The result is the same softmax up to rounding; the pages
+     * measure a coherent bf16 gain error on rows dominated by one key that is
+     * processed last.  Not part of the metadata signature. */
+    float rescale_threshold;
 } mla_problem_t;
 
 /* Split-KV schedule for one problem shape.  ``mla_plan`` fills everything

@@ -47,13 +47,14 @@ def abi_version():
 
 
 def make_problem(batch, s_q, h_q, num_blocks, max_blocks_per_seq=0, *, topk=0, causal=False, kv_format="bf16",
-                 out_dtype="bf16", softmax_scale=None):
+                 out_dtype="bf16", softmax_scale=None, rescale_threshold=0.0):
     p = Problem()
     p.batch, p.s_q, p.h_q, p.h_kv, p.d_qk, p.d_v, p.block_size = batch, s_q, h_q, 1, 576, 512, 64
     p.num_blocks, p.max_blocks_per_seq, p.topk, p.causal = num_blocks, max_blocks_per_seq, topk, int(bool(causal))
     p.kv_format = {"bf16": _lib.KV_BF16_576, "fp8": _lib.KV_FP8_656}[kv_format]
     p.out_dtype = {"bf16": _lib.OUT_BF16, "fp32": _lib.OUT_FP32}[out_dtype]
     p.softmax_scale = 1.0 / math.sqrt(576) if softmax_scale is None else float(softmax_scale)
+    p.rescale_threshold = float(rescale_threshold)
     return p
 
 
@@ -189,9 +190,10 @@ class Decoder:
         return self.decode(q, kv_cache, block_table, cache_seqlens, indices, stream)
 
     @classmethod
-    def for_workload(cls, w, device="cuda", num_cus=0):
+    def for_workload(cls, w, device="cuda", num_cus=0, rescale_threshold=0.0):
         p = make_problem(w.batch, w.s_q, w.h_q, w.num_blocks, w.max_blocks_per_seq, topk=w.topk, causal=w.causal,
-                         kv_format=w.kv_format, out_dtype=w.out_dtype, softmax_scale=w.softmax_scale)
+                         kv_format=w.kv_format, out_dtype=w.out_dtype, softmax_scale=w.softmax_scale,
+                         rescale_threshold=rescale_threshold)
         return cls(p, device, num_cus)
 
     def run_workload(self, w, stream=None):

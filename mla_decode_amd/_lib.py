@@ -10,6 +10,7 @@ import os
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libmla_decode.so")
 
+ABI_VERSION = 2   # MLA_DECODE_ABI_VERSION of the header this binding mirrors
 MLA_OK = 0
 STATUS_NAMES = {0: "MLA_OK", 1: "MLA_ERR_INVALID_ARG", 2: "MLA_ERR_UNSUPPORTED", 3: "MLA_ERR_WORKSPACE_TOO_SMALL",
                 4: "MLA_ERR_METADATA_MISMATCH", 5: "MLA_ERR_HIP"}
@@ -26,7 +27,8 @@ EXPORTED = ("mla_abi_version", "mla_status_string", "mla_plan", "mla_workspace_b
 class Problem(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "batch", "s_q", "h_q", "h_kv", "d_qk", "d_v", "block_size", "num_blocks", "max_blocks_per_seq",
-        "topk", "causal", "kv_format", "out_dtype")] + [("softmax_scale", ctypes.c_float)]
+        "topk", "causal", "kv_format", "out_dtype")] + [("softmax_scale", ctypes.c_float),
+                                                         ("rescale_threshold", ctypes.c_float)]
 
 
 class Metadata(ctypes.Structure):
@@ -57,6 +59,9 @@ def load():
     i32 = ctypes.c_int32
     lib.mla_abi_version.restype = i32
     lib.mla_abi_version.argtypes = []
+    if lib.mla_abi_version() != ABI_VERSION:
+        raise ImportError(f"{LIB_PATH} has ABI version {lib.mla_abi_version()}, this binding expects "
+                          f"{ABI_VERSION}; rebuild it with `python -m mla_decode_amd.build`")
     lib.mla_status_string.restype = ctypes.c_char_p
     lib.mla_status_string.argtypes = [ctypes.c_int]
     lib.mla_plan.restype = ctypes.c_int

@@ -44,6 +44,7 @@ mla_status_t validate(const mla_problem_t* p) {
     if (p->kv_format != MLA_KV_BF16_576 && p->kv_format != MLA_KV_FP8_656) return MLA_ERR_INVALID_ARG;
     if (p->out_dtype != MLA_OUT_BF16 && p->out_dtype != MLA_OUT_FP32) return MLA_ERR_INVALID_ARG;
     if (!std::isfinite(p->softmax_scale) || !(p->softmax_scale > 0.f)) return MLA_ERR_INVALID_ARG;
+    if (!(p->rescale_threshold >= 0.f && p->rescale_threshold <= 30.f)) return MLA_ERR_INVALID_ARG;
     if (p->h_kv != 1 || p->d_qk != mla::kDqk || p->d_v != mla::kDv || p->block_size != kBlock)
         return MLA_ERR_UNSUPPORTED;
     if (p->topk == 0 && p->max_blocks_per_seq < 1) return MLA_ERR_INVALID_ARG;
@@ -123,6 +124,7 @@ mla_status_t run_decode(const mla_problem_t* p, bool sparse, const void* q, cons
     a.n_hblk = meta->num_head_blocks;
     a.max_slots = (int)slots;
     a.scale_log2 = p->softmax_scale * 1.4426950408889634f;
+    a.rescale_tau = p->rescale_threshold;
     hipStream_t s = (hipStream_t)stream;
     if (mla::launch_decode(a, sparse, p->kv_format == MLA_KV_FP8_656, s) != hipSuccess) return MLA_ERR_HIP;
 

@@ -627,7 +627,10 @@ __global__ void __launch_bounds__(kThreads, 1) decode_kernel(const DecodeArgs a)
             mx = wave_max_pair(mx);
             fill_piece(fc, IntC<2>{});
             fill_piece(fc, IntC<3>{});
-            const float m_new = fmaxf(m_run, mx);
+            // Running max: raised to the tile max only when that exceeds it by
+            // more than tau in log2 units (tau = 0: whenever it is larger,
+            // the exact running max).  From -inf any finite max is taken.
+            const float m_new = c * (mx - m_run) <= a.rescale_tau ? m_run : fmaxf(m_run, mx);
             // while every score so far is masked, m_new = -inf: p = exp2(-inf) = 0
             const float cm = m_new == -INFINITY ? 0.f : c * m_new;
             const float alpha = __builtin_amdgcn_exp2f(c * m_run - cm);

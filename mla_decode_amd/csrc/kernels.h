@@ -21,6 +21,7 @@ struct DecodeArgs {
     int batch, s_q, h_q, max_blocks, topk, causal, out_fp32;
     int num_parts, n_hblk, max_slots;
     float scale_log2;            // softmax_scale * log2(e)
+    float rescale_tau;           // running-max threshold in log2 units (0 = exact running max)
 };
 
 struct MetaArgs {

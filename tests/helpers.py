@@ -28,9 +28,9 @@ def kv_host(w):
     return w.kv.detach().contiguous().cpu().numpy().reshape(-1, 656)
 
 
-def run_library(w, num_cus=0, stream=None):
+def run_library(w, num_cus=0, stream=None, rescale_threshold=0.0):
     import mla_decode_amd as mla
-    dec = mla.Decoder.for_workload(w, w.q.device, num_cus)
+    dec = mla.Decoder.for_workload(w, w.q.device, num_cus, rescale_threshold=rescale_threshold)
     out, lse = dec.run_workload(w, stream)
     torch.cuda.synchronize()
     return out.float().cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64), dec

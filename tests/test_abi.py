@@ -35,7 +35,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_abi_version_and_status_strings(lib):
-    assert lib.mla_abi_version() == 1
+    assert lib.mla_abi_version() == 2
     for s in range(6):
         assert lib.mla_status_string(s)
     assert lib.mla_status_string(99) == b"unknown status"
@@ -60,12 +60,29 @@ def test_plan_host_only():
     assert m.num_head_blocks == 2 and m.num_partitions == 128
     m = mla.plan(_problem(h_q=16, batch=2, num_blocks=8, max_blocks_per_seq=4), num_cus=256)
     assert m.num_head_blocks == 1 and m.num_partitions == 256
+    for tau in (0.0, 6.0, 8.0, 30.0):   # lazy-rescale thresholds in range
+        assert mla.plan(_problem(rescale_threshold=tau), num_cus=256).num_partitions == 256
+
+
+def test_struct_layout_matches_header():
+    """The ctypes Problem mirrors mla_problem_t: 13 int32 fields then two floats."""
+    from mla_decode_amd import _lib
+    names = [f[0] for f in _lib.Problem._fields_]
+    assert names[-2:] == ["softmax_scale", "rescale_threshold"]
+    assert ctypes.sizeof(_lib.Problem) == 15 * 4
+    src = open(os.path.join(ROOT, "include", "mla_decode.h")).read()
+    body = src[src.index("typedef struct {\n    int32_t batch;"):src.index("} mla_problem_t;")]
+    fields = re.findall(r"^\s*(int32_t|float)\s+(\w+);", body, flags=re.M)
+    assert [n for _, n in fields] == names
+    assert [t for t, _ in fields] == ["int32_t"] * 13 + ["float"] * 2
 
 
 @pytest.mark.parametrize("kw,status", [
     (dict(batch=0), 1), (dict(s_q=0), 1), (dict(h_q=0), 1), (dict(num_blocks=0), 1),
     (dict(max_blocks_per_seq=0), 1), (dict(topk=-1), 1), (dict(softmax_scale=float("nan")), 1), (dict(softmax_scale=0.0), 1), (dict(softmax_scale=-0.5), 1),
     (dict(topk=64, causal=True), 2), (dict(batch=20000), 2),
+    (dict(rescale_threshold=-1.0), 1), (dict(rescale_threshold=30.5), 1), (dict(rescale_threshold=float("nan")), 1),
+    (dict(rescale_threshold=float("inf")), 1),
 ])
 def test_plan_rejects(kw, status):
     import mla_decode_amd as mla
