@@ -6,6 +6,11 @@ scheduler (mla_get_decode_metadata) followed by the decode call
 decode shape b=64, s_q=1, h_q=128, seqlen=4096 (64-token pages shuffled over
 a 4096-page pool, bf16 N(0,1) inputs, inputs resident in HBM).
 
+``--workload fp8_sparse_topk2048`` / ``fp8_sparse_topk32768`` time instead
+the FP8 sparse decode shape the pages quote for their H800 kernel (b=128,
+s_q=2, h_q=128, top-k 2048 or 32768 over 656-byte records,
+mla_sparse_decode_fwd); that line's roofline is the MFMA one.
+
 Prints one JSON line.  ``value`` is TFLOP/s of algorithmic work (FLOPs =
 2 h_q (576 + 512) per visible query-token/KV-token pair) per step; the line
 also carries HBM GB/s and microseconds per step, the roofline of the decode
@@ -50,6 +55,37 @@ def measured_traffic():
     return c.get("hbm_bytes_per_launch")
 
 
+def cpu_baseline_sparse(w):
+    """The fp64 oracle on a bounded sample of a top-k workload: query tokens in
+    order, each over its gathered rows, until about 10 s of CPU work."""
+    import numpy as np
+    import threadpoolctl
+    import torch
+    from oracle import attention as A
+    q = w.q.cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
+    kv_rows = w.kv.view(-1, w.kv.shape[-1])
+    nrows = kv_rows.shape[0]
+    idx = w.indices.cpu().numpy()
+    threads = max(i.get("num_threads", 1) for i in threadpoolctl.threadpool_info() if i.get("user_api") == "blas")
+    done, flops, dt = 0, 0.0, 0.0
+    for b in range(w.batch):
+        for i in range(w.s_q):
+            rows = idx[b, i][(idx[b, i] >= 0) & (idx[b, i] < nrows)]
+            kv = kv_rows[torch.from_numpy(rows.astype(np.int64)).to(w.kv.device)].cpu().numpy()   # gathered on the GPU
+            t0 = time.perf_counter()
+            A.decode_partial(q, kv, w.softmax_scale, np.arange(len(rows)), b, i, kv_format=w.kv_format)
+            dt += time.perf_counter() - t0
+            flops += 2.0 * w.h_q * (576 + 512) * len(rows)
+            done += 1
+            if dt >= 10.0:
+                break
+        if dt >= 10.0:
+            break
+    return {"value": flops / dt / 1e12, "unit": "TFLOPS", "cores": int(threads), "kind": "oracle",
+            "sample": f"{done} of {w.batch * w.s_q} query tokens (all {w.h_q} heads x top-k {w.topk} rows each), "
+                      f"fp64 numpy, {dt:.1f} s in total"}
+
+
 def cpu_baseline(w, flops):
     """The fp64 oracle on the same workload, on this host's cores."""
     import numpy as np
@@ -79,6 +115,9 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--workload", default="dense_b64_s4096",
+                    choices=["dense_b64_s4096", "fp8_sparse_topk2048", "fp8_sparse_topk32768"],
+                    help="dense_b64_s4096 is the headline line; the others time the pages' FP8 sparse shape")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a 1 GiB device copy 5 times (reference for HBM byte counters)")
     args = ap.parse_args()
@@ -99,18 +138,23 @@ def main():
 
     import torch
     import mla_decode_amd as mla
-    from workloads import make_config, flops_and_bytes
+    from workloads import make_config, make_fp8_sparse, flops_and_bytes
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = torch.device("cuda:0")
-    w = make_config(2, device=dev)
+    headline = args.workload == "dense_b64_s4096"
+    if headline:
+        w = make_config(2, device=dev)
+    else:
+        w = make_fp8_sparse(int(args.workload.split("topk")[1]), device=dev)
     acct = flops_and_bytes(w)
     dec = mla.Decoder.for_workload(w, dev)
     stream = torch.cuda.current_stream(dev)
+    seqlens = None if w.topk else w.cache_seqlens
 
     def step():
-        dec.metadata(w.cache_seqlens, stream)
-        dec.decode(w.q, w.kv, w.block_table, w.cache_seqlens, None, stream)
+        dec.metadata(seqlens, stream)
+        dec.decode(w.q, w.kv, w.block_table, w.cache_seqlens, w.indices, stream)
 
     for _ in range(args.warmup):
         step()
@@ -133,7 +177,7 @@ def main():
     torch.cuda.synchronize()
     k0.record(stream)
     for _ in range(args.steps):
-        dec.decode(w.q, w.kv, w.block_table, w.cache_seqlens, None, stream)
+        dec.decode(w.q, w.kv, w.block_table, w.cache_seqlens, w.indices, stream)
     k1.record(stream)
     torch.cuda.synchronize()
     ms_decode = k0.elapsed_time(k1) / args.steps
@@ -145,7 +189,7 @@ def main():
     torch.cuda.synchronize()
     p0.record(stream)
     for _ in range(args.steps):
-        dec.decode_partial(w.q, w.kv, w.block_table, w.cache_seqlens, None, stream)
+        dec.decode_partial(w.q, w.kv, w.block_table, w.cache_seqlens, w.indices, stream)
     p1.record(stream)
     torch.cuda.synchronize()
     ms_kernel = p0.elapsed_time(p1) / args.steps
@@ -155,7 +199,7 @@ def main():
     m1 = torch.cuda.Event(enable_timing=True)
     m0.record(stream)
     for _ in range(args.steps):
-        dec.metadata(w.cache_seqlens, stream)
+        dec.metadata(seqlens, stream)
     m1.record(stream)
     torch.cuda.synchronize()
     ms_meta = m0.elapsed_time(m1) / args.steps
@@ -193,8 +237,23 @@ def main():
         "decode_call_us": round(ms_decode * 1e3, 2),
         "metadata_us": round(ms_meta * 1e3, 2),
     }
+    if not headline:
+        topk = w.topk
+        line["metric"] = f"MLA sparse FP8 decode TFLOPS, µs/step at b=128,s_q=2,h_q=128,topk={topk} (1 GPU)"
+        line["config"] = {"workload": f"FP8 sparse absorbed-MLA decode b=128 s_q=2 h_q=128 top-k {topk} "
+                                      f"(656-byte records, {max(32768, 2 * topk)} cached tokens per request, "
+                                      "every slot valid, N(0,1) sources)",
+                          "batch": w.batch, "s_q": w.s_q, "h_q": w.h_q, "topk": topk, "d_qk": 576, "d_v": 512,
+                          "block_size": 64, "kv_format": "fp8_656", "step": "metadata + sparse decode (partial + combine)"}
+        line["roofline"] = {"bound": "mfma", "kernel": "decode_kernel<sparse, fp8 cache> (partial attention)",
+                            "achieved": round(kern_tflops, 1), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                            "frac": round(kern_tflops / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
+                            "algorithmic_flops": flops, "us_per_launch": round(ms_kernel * 1e3, 2)}
+        line["roofline_hbm"] = {"achieved": round(kern_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                "frac": round(kern_gbs / HBM_PEAK_GBS, 4), "algorithmic_bytes_per_launch": kbytes}
+        del line["roofline_mfma"]
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(w, flops)
+        line["cpu_baseline"] = cpu_baseline(w, flops) if headline else cpu_baseline_sparse(w)
     print(json.dumps(line), flush=True)
 
 

@@ -84,6 +84,19 @@ mla_status_t check_meta(const mla_problem_t* p, const mla_metadata_t* m) {
     return MLA_OK;
 }
 
+// Top-k items all cost ceil(topk/64) + F scheduler units, so the plan alone
+// fixes the schedule.  When the partition size q = ceil(T/P) is a multiple of
+// that cost, every partition boundary falls on an item boundary: no item is
+// split and the decode kernel writes every output itself.  (A sufficient
+// condition; otherwise the combine runs and merges whatever was split.)
+bool sparse_items_whole(const mla_problem_t* p, const mla_metadata_t* m) {
+    if (p->topk <= 0) return false;
+    const int64_t cost = ((int64_t)p->topk + 63) / 64 + m->fixed_overhead;
+    const int64_t total = (int64_t)p->batch * p->s_q * cost;
+    const int64_t q = total > 0 ? (total + m->num_partitions - 1) / m->num_partitions : 1;
+    return q % cost == 0;
+}
+
 mla_status_t run_decode(const mla_problem_t* p, bool sparse, const void* q, const void* kv,
                         const int32_t* block_table, const int32_t* cache_seqlens, const int32_t* indices,
                         const mla_metadata_t* meta, void* ws, size_t ws_bytes, void* out, float* lse,
@@ -139,7 +152,7 @@ mla_status_t run_decode(const mla_problem_t* p, bool sparse, const void* q, cons
     c.s_q = p->s_q;
     c.out_fp32 = a.out_fp32;
     c.skip_single = 1;
-    if (run_combine && mla::launch_combine(c, s) != hipSuccess) return MLA_ERR_HIP;
+    if (run_combine && !sparse_items_whole(p, meta) && mla::launch_combine(c, s) != hipSuccess) return MLA_ERR_HIP;
     return MLA_OK;
 }
 

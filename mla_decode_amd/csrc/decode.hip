@@ -166,10 +166,22 @@ __device__ __forceinline__ void dma_raw_x1(const i32x4& rs, int voff, int lds) {
     __asm__ volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, 0 offen offset:%3 lds"
                      :: "s"(lds - IMM), "v"(voff), "s"(rs), "i"(IMM) : "memory", "m0");
 }
-__device__ __forceinline__ void dma_struct_x1(const i32x4& rs, int row, int voff, int lds) {
-    const i32x2 va = {row, voff};
-    __asm__ volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, 0 idxen offen lds"
-                     :: "s"(lds), "v"(va), "s"(rs) : "memory", "m0");
+// Gathered rows (sparse FP8) are copied with a 64-bit address per lane, so
+// caches beyond 4 GiB are reached (a buffer offset is 32-bit); LDS address =
+// M0 + 16 * lane (x4) or M0 + 4 * lane (x1).  An invalid row reads the zero
+// row below instead, so its bytes land as zeros like an out-of-range buffer
+// load.
+__device__ __align__(16) unsigned char g_zero_row[kFp8RowBytes];   // never written
+__device__ __forceinline__ void dma_global_x4(const unsigned char* src, int lds) {
+    __asm__ volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off"
+                     :: "s"(lds), "v"(src) : "memory", "m0");
+}
+__device__ __forceinline__ void dma_global_x1(const unsigned char* src, int lds) {
+    __asm__ volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, off"
+                     :: "s"(lds), "v"(src) : "memory", "m0");
+}
+__device__ __forceinline__ const unsigned char* fp8_row_addr(const unsigned char* kv, int row, int off) {
+    return (row >= 0 ? kv + (int64_t)row * kFp8RowBytes : g_zero_row) + off;
 }
 
 // LDS token slot of lane l in a copy of columns (c, c+1): column c + (l >> 5),
@@ -309,7 +321,6 @@ __global__ void __launch_bounds__(kThreads, 1) decode_kernel(const DecodeArgs a)
     const bool head_ok = head < H;
 
     const i32x4 srs = buffer_rsrc(kv, kRowBytes, (int)a.num_rows);
-    const i32x4 srs8 = buffer_rsrc(kv, kFp8RowBytes, (int)a.num_rows);   // FP8 sparse: one record per row
     const int ftok = l32 ^ (4 * half + 8 * (wave & 1));   // bf16 fill: token this lane copies
     const int fbase = ftok * kRowBytes + 16 * half;       // dense fill source offset (+32k)
     const int fcol = 16 * half;                            // sparse fill column offset (+32k)
@@ -440,10 +451,10 @@ __global__ void __launch_bounds__(kThreads, 1) decode_kernel(const DecodeArgs a)
                 const int rc = live ? sm.rows[it & 3][tc] : -1;
                 const int rr_ = live ? sm.rows[it & 3][tr] : -1;
                 const int rs_ = (live && l < kSubTok) ? sm.rows[it & 3][l] : -1;
-                dma_struct_x4<0>(srs8, rc, code_off, code_lds);
-                dma_struct_x4<32>(srs8, rc, code_off, code_lds + 2048);
-                dma_struct_x4<0>(srs8, rr_, rope_off, rope_lds);
-                dma_struct_x1(srs8, rs_, scale_off, sdst);
+                dma_global_x4(fp8_row_addr(kv, rc, code_off), code_lds);
+                dma_global_x4(fp8_row_addr(kv, rc, code_off + 32), code_lds + 2048);
+                dma_global_x4(fp8_row_addr(kv, rr_, rope_off), rope_lds);
+                dma_global_x1(fp8_row_addr(kv, rs_, scale_off), sdst);
             } else {
                 const bool ok = it < ns && page_ok(page, a.num_rows);
                 int nvalid = min(nslots - g * kSubTok, kSubTok);

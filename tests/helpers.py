@@ -28,6 +28,21 @@ def kv_host(w):
     return w.kv.detach().contiguous().cpu().numpy().reshape(-1, 656)
 
 
+def kv_host_rows(w, items):
+    """Host copy of the cache holding only the rows the sampled top-k query
+    tokens gather (the rest stay zero pages of a lazily allocated array), so
+    that multi-GB caches need not be copied whole."""
+    rows_dev = w.kv.view(-1, w.kv.shape[-1])
+    nrows = rows_dev.shape[0]
+    idx = w.indices.cpu().numpy()
+    need = np.unique(np.concatenate([idx[b, i][(idx[b, i] >= 0) & (idx[b, i] < nrows)] for b, i in items]))
+    host = np.zeros((nrows, rows_dev.shape[1]), dtype=np.uint8 if w.kv_format == 'fp8' else np.uint16)
+    sel = torch.from_numpy(need.astype(np.int64)).to(w.kv.device)
+    got = rows_dev[sel].cpu()
+    host[need] = got.numpy() if w.kv_format == 'fp8' else got.view(torch.int16).numpy().view(np.uint16)
+    return host
+
+
 def run_library(w, num_cus=0, stream=None, rescale_threshold=0.0):
     import mla_decode_amd as mla
     dec = mla.Decoder.for_workload(w, w.q.device, num_cus, rescale_threshold=rescale_threshold)

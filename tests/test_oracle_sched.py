@@ -84,3 +84,27 @@ def test_causal_tiles():
     assert S.item_tiles_dense([64], 2, False).tolist() == [1, 1]
     assert S.item_tiles_sparse(2, 1, 2048).tolist() == [32, 32]
     assert S.item_tiles_sparse(1, 2, 100).tolist() == [2, 2]
+
+
+def test_sparse_whole_item_rule():
+    """The decode call skips the combine launch for a top-k problem when the
+    partition size q is a multiple of the per-item cost.  Checked against the
+    scheduler: the rule never fires when some item is split, and it does fire
+    on the pages' FP8 sparse shapes (b=128, s_q=2, top-k 2048 and 32768, 256
+    partitions), where every item is whole."""
+    fired = 0
+    for batch in (1, 2, 3, 5, 8, 64, 128):
+        for s_q in (1, 2):
+            for topk in (1, 63, 64, 100, 2048, 5000):
+                for P in (1, 3, 8, 64, 256):
+                    n = S.item_tiles_sparse(batch, s_q, topk)
+                    sch = S.schedule(n, P, 0)
+                    cost = int(n[0])
+                    if sch['q'] % cost == 0:
+                        fired += 1
+                        assert (sch['num_splits'] == 1).all(), (batch, s_q, topk, P)
+    assert fired > 50
+    for topk in (2048, 32768):
+        n = S.item_tiles_sparse(128, 2, topk)
+        sch = S.schedule(n, 256, 0)
+        assert sch['q'] % int(n[0]) == 0 and (sch['num_splits'] == 1).all()

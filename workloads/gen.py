@@ -216,6 +216,17 @@ def make_sparse(batch, s_q, h_q, *, pool_tokens_per_seq, topk, invalid_frac=0.05
                     indices=indices, meta={'peaked': peaked, 'order': order})
 
 
+def make_fp8_sparse(topk, device='cpu', seed=None, batch=128, s_q=2, h_q=128):
+    """The FP8 sparse decode shape the pages quote for the H800 kernel: 128
+    requests, 2 query tokens each, 128 heads, top-k 2048 or 32768 over a
+    656-byte record cache.  Every slot is valid; each request holds
+    max(32768, 2 topk) cached tokens to choose from."""
+    seed = 2000 + topk if seed is None else seed
+    pool = max(32768, 2 * topk)
+    return make_sparse(batch, s_q, h_q, pool_tokens_per_seq=pool, topk=topk, invalid_frac=0.0, seed=seed,
+                       device=device, kv_format='fp8', name=f'fp8_sparse_b{batch}_s{s_q}_topk{topk}')
+
+
 def make_config(i, device='cpu', seed=None, **kw):
     """The five workloads, with seed 1000 + i unless given."""
     seed = 1000 + i if seed is None else seed
