@@ -17,6 +17,15 @@
  * requested; sparse: the valid top-k indices).  A query that sees no token
  * gets out = 0 and lse = -inf.
  *
+ * Optional arguments (FlashMLA README, sparse attention arguments):
+ *  - attn_sink [h_q] float32: a per-head sink logit; every output row is
+ *    scaled by exp(lse) / (exp(lse) + exp(attn_sink[h])).  lse itself is
+ *    unchanged.  NULL: no sink.
+ *  - topk_length [batch, s_q] int32 (sparse only): query token (b, i) attends
+ *    only to its first topk_length[b, i] index entries (values are clamped
+ *    to [0, topk]).  NULL: all topk entries.  The README gives the argument
+ *    per query token of its prefill call; here it is per decode query token.
+ *
  * Conventions for every entry point:
  *  - Device pointers point to contiguous, row-major device memory owned by the
  *    caller; the library allocates no device memory and keeps no state other
@@ -131,23 +140,27 @@ mla_status_t mla_plan(const mla_problem_t *problem, int32_t num_cus, mla_metadat
 size_t mla_workspace_bytes(const mla_metadata_t *meta);
 
 /* Split-KV tile scheduler.  Writes meta->dev on ``stream`` from
- * cache_seqlens (device, [batch]; ignored and may be NULL when topk > 0).
+ * cache_seqlens (device, [batch]; dense only, ignored and may be NULL when
+ * topk > 0) or, for sparse problems, topk_length (device, [batch, s_q], or
+ * NULL when every query token uses all topk entries; ignored when dense).
+ * The decode call must be given the same topk_length.
  * The scheduler balances KV tiles of 64 tokens (plus a fixed per-item cost)
  * over the partitions in contiguous ranges (FlashMLA new-kernel deep dive,
  * "Other performance improvements": the tile scheduler spreads requests and
  * blocks evenly over the compute units).  Errors: INVALID_ARG, UNSUPPORTED,
  * METADATA_MISMATCH if meta was planned for another problem, HIP. */
 mla_status_t mla_get_decode_metadata(const mla_problem_t *problem, const int32_t *cache_seqlens,
-                                     mla_metadata_t *meta, void *stream);
+                                     const int32_t *topk_length, mla_metadata_t *meta, void *stream);
 
 /* Dense decode over the paged cache through block_table and
  * cache_seqlens (both device).  problem->topk must be 0.  Writes out and lse.
  * ``workspace`` holds split partials (device, >= mla_workspace_bytes(meta)).
  * The caller keeps ``meta->dev`` current: reusing metadata made from other
  * cache_seqlens silently mis-splits (the pages give the same warning).
+ * attn_sink: device [h_q] float32 or NULL (see the top of this file).
  * Errors: INVALID_ARG, UNSUPPORTED, WORKSPACE_TOO_SMALL, METADATA_MISMATCH, HIP. */
 mla_status_t mla_decode_fwd(const mla_problem_t *problem, const void *q, const void *kv_cache,
-                            const int32_t *block_table, const int32_t *cache_seqlens,
+                            const int32_t *block_table, const int32_t *cache_seqlens, const float *attn_sink,
                             const mla_metadata_t *meta, void *workspace, size_t workspace_bytes,
                             void *out, float *lse, void *stream);
 
@@ -156,10 +169,13 @@ mla_status_t mla_decode_fwd(const mla_problem_t *problem, const void *q, const v
  * offset; block_table is not used, FlashMLA README "indices Tensor").  Entries
  * < 0 or >= num_blocks*64 are masked (the pages mark -1 invalid and do no
  * upper-bound check; this library masks instead of faulting).  problem->topk
- * must be > 0 and problem->causal 0.  Same errors as mla_decode_fwd. */
+ * must be > 0 and problem->causal 0.  topk_length (device [batch, s_q] int32
+ * or NULL) and attn_sink (device [h_q] float32 or NULL) as at the top of
+ * this file; the metadata must have been made with the same topk_length.
+ * Same errors as mla_decode_fwd. */
 mla_status_t mla_sparse_decode_fwd(const mla_problem_t *problem, const void *q, const void *kv_cache,
-                                   const int32_t *indices, const mla_metadata_t *meta,
-                                   void *workspace, size_t workspace_bytes,
+                                   const int32_t *indices, const int32_t *topk_length, const float *attn_sink,
+                                   const mla_metadata_t *meta, void *workspace, size_t workspace_bytes,
                                    void *out, float *lse, void *stream);
 
 /* LSE merge of split partials ("matrices, attention & GPU" explainer,
@@ -169,11 +185,12 @@ mla_status_t mla_sparse_decode_fwd(const mla_problem_t *problem, const void *q, 
  *   o_part   [slots, h_q, 512] float32 (normalised partial outputs)
  *   lse_part [slots, h_q]      float32 (natural-log lse, -inf = empty)
  * and receives out[b, i, :, :] and lse[b, :, i].  An item with no slot, or
- * whose partials are all -inf, gets out = 0 and lse = -inf.  All pointers are
- * device memory.  Errors: INVALID_ARG, HIP. */
+ * whose partials are all -inf, gets out = 0 and lse = -inf.  attn_sink
+ * ([h_q] float32 or NULL) scales each merged row as at the top of this file.
+ * All pointers are device memory.  Errors: INVALID_ARG, HIP. */
 mla_status_t mla_combine(int32_t num_items, int32_t h_q, int32_t s_q, const float *o_part,
-                         const float *lse_part, const int32_t *split_offsets, int32_t out_dtype,
-                         void *out, float *lse, void *stream);
+                         const float *lse_part, const int32_t *split_offsets, const float *attn_sink,
+                         int32_t out_dtype, void *out, float *lse, void *stream);
 
 /* Test hook: the partial-attention kernel of mla_decode_fwd /
  * mla_sparse_decode_fwd alone, without the LSE combine.  Items whose KV range
@@ -181,10 +198,12 @@ mla_status_t mla_combine(int32_t num_items, int32_t h_q, int32_t s_q, const floa
  * normalised partials in ``workspace`` (layout as in mla_combine: o_part
  * first, then lse_part at float offset max_splits*h_q*512) and its out/lse
  * untouched.  ``table_or_indices`` is block_table (dense) or indices (sparse);
- * cache_seqlens is ignored for sparse problems.  Same errors as
+ * cache_seqlens is ignored for sparse problems, topk_length for dense ones;
+ * attn_sink applies to the outputs this call writes.  Same errors as
  * mla_decode_fwd. */
 mla_status_t mla_debug_decode_partial(const mla_problem_t *problem, const void *q, const void *kv_cache,
                                       const int32_t *table_or_indices, const int32_t *cache_seqlens,
+                                      const int32_t *topk_length, const float *attn_sink,
                                       const mla_metadata_t *meta, void *workspace, size_t workspace_bytes,
                                       void *out, float *lse, void *stream);
 
@@ -193,9 +212,11 @@ mla_status_t mla_debug_decode_partial(const mla_problem_t *problem, const void *
  * slot is masked; rows_out is device int32 [batch*s_q, row_stride] with
  * row_stride = 64*max_blocks_per_seq (dense) or 64*ceil(topk/64) (sparse);
  * columns past an item's tiles are left untouched.  ``table_or_indices`` is
- * block_table (dense) or indices (sparse).  Errors: INVALID_ARG, UNSUPPORTED, HIP. */
+ * block_table (dense) or indices (sparse); slots past a sparse item's
+ * topk_length (when given) are masked.  Errors: INVALID_ARG, UNSUPPORTED, HIP. */
 mla_status_t mla_debug_gather_rows(const mla_problem_t *problem, const int32_t *table_or_indices,
-                                   const int32_t *cache_seqlens, int32_t *rows_out, void *stream);
+                                   const int32_t *cache_seqlens, const int32_t *topk_length,
+                                   int32_t *rows_out, void *stream);
 
 #ifdef __cplusplus
 }

@@ -70,21 +70,46 @@ def workspace_bytes(meta):
     return int(_lib.load().mla_workspace_bytes(ctypes.byref(meta)))
 
 
-def get_decode_metadata(problem, cache_seqlens, meta, meta_buf, stream=None):
-    """Split-KV scheduler: fill ``meta_buf`` (device uint8/int32 tensor >= meta.bytes) with the schedule."""
+def _optional(t, name, dtype, numel):
+    if t is None:
+        return None
+    _need(t, name, dtype)
+    if t.numel() != numel:
+        raise ValueError(f"{name} must have {numel} elements, got {t.numel()}")
+    return t
+
+
+def _topk_length(problem, topk_length):
+    """Sparse only: [batch, s_q] int32 or None; ignored (None) for dense problems."""
+    if problem.topk == 0:
+        return None
+    return _optional(topk_length, "topk_length", torch.int32, problem.batch * problem.s_q)
+
+
+def _attn_sink(h_q, attn_sink):
+    return _optional(attn_sink, "attn_sink", torch.float32, h_q)
+
+
+def get_decode_metadata(problem, cache_seqlens, meta, meta_buf, stream=None, topk_length=None):
+    """Split-KV scheduler: fill ``meta_buf`` (device uint8/int32 tensor >= meta.bytes) with the schedule.
+    Dense problems read cache_seqlens; sparse ones read topk_length (None: all topk entries)."""
     lib = _lib.load()
     _need(meta_buf, "meta_buf", None)
     if meta_buf.numel() * meta_buf.element_size() < meta.bytes:
         raise ValueError("meta_buf too small")
-    if cache_seqlens is not None:
+    if problem.topk > 0:
+        cache_seqlens = None
+    elif cache_seqlens is not None:
         _need(cache_seqlens, "cache_seqlens", torch.int32)
+    tl = _topk_length(problem, topk_length)
     meta.dev = meta_buf.data_ptr()
     _lib.check("mla_get_decode_metadata", lib.mla_get_decode_metadata(
-        ctypes.byref(problem), _ptr(cache_seqlens), ctypes.byref(meta), _stream(stream)))
+        ctypes.byref(problem), _ptr(cache_seqlens), _ptr(tl), ctypes.byref(meta), _stream(stream)))
     return meta
 
 
-def decode_fwd(problem, q, kv_cache, block_table, cache_seqlens, meta, workspace, out, lse, stream=None):
+def decode_fwd(problem, q, kv_cache, block_table, cache_seqlens, meta, workspace, out, lse, stream=None,
+               attn_sink=None):
     """Dense paged decode (mla_decode_fwd)."""
     lib = _lib.load()
     _need(q, "q", torch.bfloat16)
@@ -94,13 +119,15 @@ def decode_fwd(problem, q, kv_cache, block_table, cache_seqlens, meta, workspace
     _need(workspace, "workspace", None)
     _need(out, "out", None)
     _need(lse, "lse", torch.float32)
+    sink = _attn_sink(problem.h_q, attn_sink)
     _lib.check("mla_decode_fwd", lib.mla_decode_fwd(
-        ctypes.byref(problem), _ptr(q), _ptr(kv_cache), _ptr(block_table), _ptr(cache_seqlens),
+        ctypes.byref(problem), _ptr(q), _ptr(kv_cache), _ptr(block_table), _ptr(cache_seqlens), _ptr(sink),
         ctypes.byref(meta), _ptr(workspace), workspace.numel() * workspace.element_size(), _ptr(out), _ptr(lse),
         _stream(stream)))
 
 
-def sparse_decode_fwd(problem, q, kv_cache, indices, meta, workspace, out, lse, stream=None):
+def sparse_decode_fwd(problem, q, kv_cache, indices, meta, workspace, out, lse, stream=None, topk_length=None,
+                      attn_sink=None):
     """Top-k sparse decode (mla_sparse_decode_fwd)."""
     lib = _lib.load()
     _need(q, "q", torch.bfloat16)
@@ -109,12 +136,14 @@ def sparse_decode_fwd(problem, q, kv_cache, indices, meta, workspace, out, lse, 
     _need(workspace, "workspace", None)
     _need(out, "out", None)
     _need(lse, "lse", torch.float32)
+    tl, sink = _topk_length(problem, topk_length), _attn_sink(problem.h_q, attn_sink)
     _lib.check("mla_sparse_decode_fwd", lib.mla_sparse_decode_fwd(
-        ctypes.byref(problem), _ptr(q), _ptr(kv_cache), _ptr(indices), ctypes.byref(meta), _ptr(workspace),
+        ctypes.byref(problem), _ptr(q), _ptr(kv_cache), _ptr(indices), _ptr(tl), _ptr(sink), ctypes.byref(meta),
+        _ptr(workspace),
         workspace.numel() * workspace.element_size(), _ptr(out), _ptr(lse), _stream(stream)))
 
 
-def combine(num_items, h_q, s_q, o_part, lse_part, split_offsets, out, lse, stream=None):
+def combine(num_items, h_q, s_q, o_part, lse_part, split_offsets, out, lse, stream=None, attn_sink=None):
     """Standalone LSE merge of split partials (mla_combine)."""
     lib = _lib.load()
     _need(o_part, "o_part", torch.float32)
@@ -123,20 +152,24 @@ def combine(num_items, h_q, s_q, o_part, lse_part, split_offsets, out, lse, stre
     _need(out, "out", None)
     _need(lse, "lse", torch.float32)
     od = {torch.bfloat16: _lib.OUT_BF16, torch.float32: _lib.OUT_FP32}[out.dtype]
+    sink = _attn_sink(int(h_q), attn_sink)
     _lib.check("mla_combine", lib.mla_combine(int(num_items), int(h_q), int(s_q), _ptr(o_part), _ptr(lse_part),
-                                              _ptr(split_offsets), od, _ptr(out), _ptr(lse), _stream(stream)))
+                                              _ptr(split_offsets), _ptr(sink), od, _ptr(out), _ptr(lse),
+                                              _stream(stream)))
 
 
-def debug_gather_rows(problem, table_or_indices, cache_seqlens, rows_out, stream=None):
+def debug_gather_rows(problem, table_or_indices, cache_seqlens, rows_out, stream=None, topk_length=None):
     lib = _lib.load()
     _need(table_or_indices, "table_or_indices", torch.int32)
     _need(rows_out, "rows_out", torch.int32)
+    tl = _topk_length(problem, topk_length)
     _lib.check("mla_debug_gather_rows", lib.mla_debug_gather_rows(
-        ctypes.byref(problem), _ptr(table_or_indices), _ptr(cache_seqlens), _ptr(rows_out), _stream(stream)))
+        ctypes.byref(problem), _ptr(table_or_indices), _ptr(cache_seqlens), _ptr(tl), _ptr(rows_out),
+        _stream(stream)))
 
 
 def debug_decode_partial(problem, q, kv_cache, table_or_indices, cache_seqlens, meta, workspace, out, lse,
-                         stream=None):
+                         stream=None, topk_length=None, attn_sink=None):
     """Test hook: the partial-attention kernel alone (mla_debug_decode_partial)."""
     lib = _lib.load()
     _need(q, "q", torch.bfloat16)
@@ -145,9 +178,10 @@ def debug_decode_partial(problem, q, kv_cache, table_or_indices, cache_seqlens, 
     _need(workspace, "workspace", None)
     _need(out, "out", None)
     _need(lse, "lse", torch.float32)
+    tl, sink = _topk_length(problem, topk_length), _attn_sink(problem.h_q, attn_sink)
     _lib.check("mla_debug_decode_partial", lib.mla_debug_decode_partial(
-        ctypes.byref(problem), _ptr(q), _ptr(kv_cache), _ptr(table_or_indices), _ptr(cache_seqlens),
-        ctypes.byref(meta), _ptr(workspace), workspace.numel() * workspace.element_size(), _ptr(out), _ptr(lse),
+        ctypes.byref(problem), _ptr(q), _ptr(kv_cache), _ptr(table_or_indices), _ptr(cache_seqlens), _ptr(tl),
+        _ptr(sink), ctypes.byref(meta), _ptr(workspace), workspace.numel() * workspace.element_size(), _ptr(out), _ptr(lse),
         _stream(stream)))
 
 
@@ -167,27 +201,30 @@ class Decoder:
         self.out = torch.empty((B, S, H, 512), dtype=odt, device=dev)
         self.lse = torch.empty((B, H, S), dtype=torch.float32, device=dev)
 
-    def metadata(self, cache_seqlens=None, stream=None):
-        get_decode_metadata(self.problem, cache_seqlens, self.meta, self.meta_buf, stream)
+    def metadata(self, cache_seqlens=None, stream=None, topk_length=None):
+        get_decode_metadata(self.problem, cache_seqlens, self.meta, self.meta_buf, stream, topk_length)
 
-    def decode_partial(self, q, kv_cache, block_table=None, cache_seqlens=None, indices=None, stream=None):
+    def decode_partial(self, q, kv_cache, block_table=None, cache_seqlens=None, indices=None, stream=None,
+                       topk_length=None, attn_sink=None):
         """The partial-attention kernel alone (test and measurement hook)."""
         toi = indices if self.problem.topk > 0 else block_table
         debug_decode_partial(self.problem, q, kv_cache, toi, cache_seqlens, self.meta, self.workspace, self.out,
-                             self.lse, stream)
+                             self.lse, stream, topk_length, attn_sink)
 
-    def decode(self, q, kv_cache, block_table=None, cache_seqlens=None, indices=None, stream=None):
+    def decode(self, q, kv_cache, block_table=None, cache_seqlens=None, indices=None, stream=None,
+               topk_length=None, attn_sink=None):
         if self.problem.topk > 0:
             sparse_decode_fwd(self.problem, q, kv_cache, indices, self.meta, self.workspace, self.out, self.lse,
-                              stream)
+                              stream, topk_length, attn_sink)
         else:
             decode_fwd(self.problem, q, kv_cache, block_table, cache_seqlens, self.meta, self.workspace, self.out,
-                       self.lse, stream)
+                       self.lse, stream, attn_sink)
         return self.out, self.lse
 
-    def step(self, q, kv_cache, block_table=None, cache_seqlens=None, indices=None, stream=None):
-        self.metadata(cache_seqlens, stream)
-        return self.decode(q, kv_cache, block_table, cache_seqlens, indices, stream)
+    def step(self, q, kv_cache, block_table=None, cache_seqlens=None, indices=None, stream=None,
+             topk_length=None, attn_sink=None):
+        self.metadata(cache_seqlens, stream, topk_length)
+        return self.decode(q, kv_cache, block_table, cache_seqlens, indices, stream, topk_length, attn_sink)
 
     @classmethod
     def for_workload(cls, w, device="cuda", num_cus=0, rescale_threshold=0.0):
@@ -197,4 +234,5 @@ class Decoder:
         return cls(p, device, num_cus)
 
     def run_workload(self, w, stream=None):
-        return self.step(w.q, w.kv, w.block_table, w.cache_seqlens, w.indices, stream)
+        return self.step(w.q, w.kv, w.block_table, w.cache_seqlens, w.indices, stream,
+                         getattr(w, "topk_length", None), getattr(w, "attn_sink", None))

@@ -69,17 +69,19 @@ def load():
     lib.mla_workspace_bytes.restype = ctypes.c_size_t
     lib.mla_workspace_bytes.argtypes = [P(Metadata)]
     lib.mla_get_decode_metadata.restype = ctypes.c_int
-    lib.mla_get_decode_metadata.argtypes = [P(Problem), vp, P(Metadata), vp]
+    lib.mla_get_decode_metadata.argtypes = [P(Problem), vp, vp, P(Metadata), vp]
     lib.mla_decode_fwd.restype = ctypes.c_int
-    lib.mla_decode_fwd.argtypes = [P(Problem), vp, vp, vp, vp, P(Metadata), vp, ctypes.c_size_t, vp, vp, vp]
+    lib.mla_decode_fwd.argtypes = [P(Problem), vp, vp, vp, vp, vp, P(Metadata), vp, ctypes.c_size_t, vp, vp, vp]
     lib.mla_sparse_decode_fwd.restype = ctypes.c_int
-    lib.mla_sparse_decode_fwd.argtypes = [P(Problem), vp, vp, vp, P(Metadata), vp, ctypes.c_size_t, vp, vp, vp]
+    lib.mla_sparse_decode_fwd.argtypes = [P(Problem), vp, vp, vp, vp, vp, P(Metadata), vp, ctypes.c_size_t, vp, vp,
+                                          vp]
     lib.mla_combine.restype = ctypes.c_int
-    lib.mla_combine.argtypes = [i32, i32, i32, vp, vp, vp, i32, vp, vp, vp]
+    lib.mla_combine.argtypes = [i32, i32, i32, vp, vp, vp, vp, i32, vp, vp, vp]
     lib.mla_debug_gather_rows.restype = ctypes.c_int
-    lib.mla_debug_gather_rows.argtypes = [P(Problem), vp, vp, vp, vp]
+    lib.mla_debug_gather_rows.argtypes = [P(Problem), vp, vp, vp, vp, vp]
     lib.mla_debug_decode_partial.restype = ctypes.c_int
-    lib.mla_debug_decode_partial.argtypes = [P(Problem), vp, vp, vp, vp, P(Metadata), vp, ctypes.c_size_t, vp, vp, vp]
+    lib.mla_debug_decode_partial.argtypes = [P(Problem), vp, vp, vp, vp, vp, vp, P(Metadata), vp, ctypes.c_size_t,
+                                             vp, vp, vp]
     _lib = lib
     return lib
 

@@ -99,7 +99,7 @@ bool sparse_items_whole(const mla_problem_t* p, const mla_metadata_t* m) {
 
 mla_status_t run_decode(const mla_problem_t* p, bool sparse, const void* q, const void* kv,
                         const int32_t* block_table, const int32_t* cache_seqlens, const int32_t* indices,
-                        const mla_metadata_t* meta, void* ws, size_t ws_bytes, void* out, float* lse,
+                        const int32_t* topk_length, const float* attn_sink, const mla_metadata_t* meta, void* ws, size_t ws_bytes, void* out, float* lse,
                         void* stream, bool run_combine = true) {
     mla_status_t st = validate(p);
     if (st != MLA_OK) return st;
@@ -120,6 +120,8 @@ mla_status_t run_decode(const mla_problem_t* p, bool sparse, const void* q, cons
     a.block_table = block_table;
     a.cache_seqlens = cache_seqlens;
     a.indices = indices;
+    a.topk_length = sparse ? topk_length : nullptr;
+    a.attn_sink = attn_sink;
     a.meta = (const int32_t*)meta->dev;
     a.o_part = (float*)ws;
     a.lse_part = (float*)ws + slots * p->h_q * mla::kDv;
@@ -145,6 +147,7 @@ mla_status_t run_decode(const mla_problem_t* p, bool sparse, const void* q, cons
     c.o_part = a.o_part;
     c.lse_part = a.lse_part;
     c.split_offsets = a.meta + mla::kMetaHeader + mla::kMetaRec * meta->num_partitions;
+    c.attn_sink = attn_sink;
     c.out = out;
     c.lse = lse;
     c.num_items = p->batch * p->s_q;
@@ -152,7 +155,8 @@ mla_status_t run_decode(const mla_problem_t* p, bool sparse, const void* q, cons
     c.s_q = p->s_q;
     c.out_fp32 = a.out_fp32;
     c.skip_single = 1;
-    if (run_combine && !sparse_items_whole(p, meta) && mla::launch_combine(c, s) != hipSuccess) return MLA_ERR_HIP;
+    const bool skip = sparse && !topk_length && sparse_items_whole(p, meta);
+    if (run_combine && !skip && mla::launch_combine(c, s) != hipSuccess) return MLA_ERR_HIP;
     return MLA_OK;
 }
 
@@ -202,14 +206,14 @@ size_t mla_workspace_bytes(const mla_metadata_t* meta) {
 }
 
 mla_status_t mla_get_decode_metadata(const mla_problem_t* problem, const int32_t* cache_seqlens,
-                                     mla_metadata_t* meta, void* stream) {
+                                     const int32_t* topk_length, mla_metadata_t* meta, void* stream) {
     mla_status_t st = validate(problem);
     if (st != MLA_OK) return st;
     st = check_meta(problem, meta);
     if (st != MLA_OK) return st;
     if (problem->topk == 0 && !cache_seqlens) return MLA_ERR_INVALID_ARG;
     mla::MetaArgs a{};
-    a.cache_seqlens = cache_seqlens;
+    a.cache_seqlens = problem->topk > 0 ? topk_length : cache_seqlens;
     a.meta = (int32_t*)meta->dev;
     a.batch = problem->batch;
     a.s_q = problem->s_q;
@@ -222,21 +226,24 @@ mla_status_t mla_get_decode_metadata(const mla_problem_t* problem, const int32_t
 }
 
 mla_status_t mla_decode_fwd(const mla_problem_t* problem, const void* q, const void* kv_cache,
-                            const int32_t* block_table, const int32_t* cache_seqlens, const mla_metadata_t* meta,
-                            void* workspace, size_t workspace_bytes, void* out, float* lse, void* stream) {
-    return run_decode(problem, false, q, kv_cache, block_table, cache_seqlens, nullptr, meta, workspace,
-                      workspace_bytes, out, lse, stream);
+                            const int32_t* block_table, const int32_t* cache_seqlens, const float* attn_sink,
+                            const mla_metadata_t* meta, void* workspace, size_t workspace_bytes, void* out,
+                            float* lse, void* stream) {
+    return run_decode(problem, false, q, kv_cache, block_table, cache_seqlens, nullptr, nullptr, attn_sink, meta,
+                      workspace, workspace_bytes, out, lse, stream);
 }
 
 mla_status_t mla_sparse_decode_fwd(const mla_problem_t* problem, const void* q, const void* kv_cache,
-                                   const int32_t* indices, const mla_metadata_t* meta, void* workspace,
-                                   size_t workspace_bytes, void* out, float* lse, void* stream) {
-    return run_decode(problem, true, q, kv_cache, nullptr, nullptr, indices, meta, workspace, workspace_bytes,
-                      out, lse, stream);
+                                   const int32_t* indices, const int32_t* topk_length, const float* attn_sink,
+                                   const mla_metadata_t* meta, void* workspace, size_t workspace_bytes, void* out,
+                                   float* lse, void* stream) {
+    return run_decode(problem, true, q, kv_cache, nullptr, nullptr, indices, topk_length, attn_sink, meta,
+                      workspace, workspace_bytes, out, lse, stream);
 }
 
 mla_status_t mla_combine(int32_t num_items, int32_t h_q, int32_t s_q, const float* o_part, const float* lse_part,
-                         const int32_t* split_offsets, int32_t out_dtype, void* out, float* lse, void* stream) {
+                         const int32_t* split_offsets, const float* attn_sink, int32_t out_dtype, void* out,
+                         float* lse, void* stream) {
     if (num_items < 1 || h_q < 1 || s_q < 1 || num_items % s_q != 0) return MLA_ERR_INVALID_ARG;
     if (!o_part || !lse_part || !split_offsets || !out || !lse) return MLA_ERR_INVALID_ARG;
     if (!aligned16(o_part) || !aligned16(out)) return MLA_ERR_INVALID_ARG;
@@ -246,6 +253,7 @@ mla_status_t mla_combine(int32_t num_items, int32_t h_q, int32_t s_q, const floa
     c.o_part = o_part;
     c.lse_part = lse_part;
     c.split_offsets = split_offsets;
+    c.attn_sink = attn_sink;
     c.out = out;
     c.lse = lse;
     c.num_items = num_items;
@@ -258,23 +266,25 @@ mla_status_t mla_combine(int32_t num_items, int32_t h_q, int32_t s_q, const floa
 
 mla_status_t mla_debug_decode_partial(const mla_problem_t* problem, const void* q, const void* kv_cache,
                                       const int32_t* table_or_indices, const int32_t* cache_seqlens,
+                                      const int32_t* topk_length, const float* attn_sink,
                                       const mla_metadata_t* meta, void* workspace, size_t workspace_bytes,
                                       void* out, float* lse, void* stream) {
     if (!problem) return MLA_ERR_INVALID_ARG;
     const bool sparse = problem->topk > 0;
     return run_decode(problem, sparse, q, kv_cache, sparse ? nullptr : table_or_indices,
-                      sparse ? nullptr : cache_seqlens, sparse ? table_or_indices : nullptr, meta, workspace,
-                      workspace_bytes, out, lse, stream, false);
+                      sparse ? nullptr : cache_seqlens, sparse ? table_or_indices : nullptr, topk_length,
+                      attn_sink, meta, workspace, workspace_bytes, out, lse, stream, false);
 }
 
 mla_status_t mla_debug_gather_rows(const mla_problem_t* problem, const int32_t* table_or_indices,
-                                   const int32_t* cache_seqlens, int32_t* rows_out, void* stream) {
+                                   const int32_t* cache_seqlens, const int32_t* topk_length, int32_t* rows_out,
+                                   void* stream) {
     mla_status_t st = validate(problem);
     if (st != MLA_OK) return st;
     if (!table_or_indices || !rows_out || (problem->topk == 0 && !cache_seqlens)) return MLA_ERR_INVALID_ARG;
     mla::GatherArgs g{};
     g.table_or_indices = table_or_indices;
-    g.cache_seqlens = cache_seqlens;
+    g.cache_seqlens = problem->topk > 0 ? topk_length : cache_seqlens;
     g.rows_out = rows_out;
     g.num_rows = (int64_t)problem->num_blocks * kBlock;
     g.batch = problem->batch;

@@ -64,6 +64,12 @@ __global__ void __launch_bounds__(256) combine_kernel(const CombineArgs a) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) o[e] *= inv;
         lse_v = m + __logf(wsum);
+        // attention sink: out is scaled by exp(lse) / (exp(lse) + exp(sink))
+        if (a.attn_sink) {
+            const float f = 1.f / (1.f + __expf(a.attn_sink[h] - lse_v));
+#pragma unroll
+            for (int e = 0; e < 8; ++e) o[e] *= f;
+        }
     } else {
 #pragma unroll
         for (int e = 0; e < 8; ++e) o[e] = 0.f;

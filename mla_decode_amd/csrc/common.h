@@ -77,27 +77,34 @@ __device__ __forceinline__ int64_t sparse_entry_row(int64_t r, int64_t num_rows)
     return (r < 0 || r >= num_rows) ? -1 : r;
 }
 
+// Top-k slots item j attends to: its first topk_length[j] entries (clamped to
+// [0, topk]), or all topk without a length array.
+__device__ __forceinline__ int topk_slots(int len, int topk) {
+    return len < 0 ? 0 : (len > topk ? topk : len);
+}
+
 struct RowResolver {
     const int32_t* block_table;    // dense
-    const int32_t* cache_seqlens;  // dense
+    const int32_t* lengths;        // dense: cache_seqlens [batch]; sparse: topk_length [batch*s_q] or null
     const int32_t* indices;        // sparse
     int s_q, max_blocks, topk, causal;
     int64_t num_rows;
 
-    // number of KV slots of item j (dense: causal-visible tokens; sparse: topk)
+    // number of KV slots of item j (dense: causal-visible tokens; sparse: topk
+    // or the item's top-k length)
     __device__ __forceinline__ int slots(int j) const {
-        if (topk > 0) return topk;
+        if (topk > 0) return lengths ? topk_slots(lengths[j], topk) : topk;
         int b = j / s_q, i = j - b * s_q;
-        return visible_len(clamp_len(cache_seqlens[b], max_blocks), s_q, i, causal);
+        return visible_len(clamp_len(lengths[b], max_blocks), s_q, i, causal);
     }
     __device__ __forceinline__ int page(int j, int tile) const {
         return block_table[(int64_t)(j / s_q) * max_blocks + tile];
     }
     // wave-uniform variants (scalar loads)
     __device__ __forceinline__ int slots_uniform(int j) const {
-        if (topk > 0) return topk;
+        if (topk > 0) return lengths ? topk_slots(sload(lengths + j), topk) : topk;
         int b = j / s_q, i = j - b * s_q;
-        return visible_len(clamp_len(sload(cache_seqlens + b), max_blocks), s_q, i, causal);
+        return visible_len(clamp_len(sload(lengths + b), max_blocks), s_q, i, causal);
     }
     __device__ __forceinline__ int page_uniform(int j, int tile) const {
         return sload(block_table + (int64_t)(j / s_q) * max_blocks + tile);

@@ -314,7 +314,8 @@ __global__ void __launch_bounds__(kThreads, 1) decode_kernel(const DecodeArgs a)
     const float c = a.scale_log2;
     const unsigned char* kv = (const unsigned char*)a.kv;
 
-    RowResolver rr{a.block_table, a.cache_seqlens, a.indices, a.s_q, a.max_blocks, SPARSE ? a.topk : 0,
+    RowResolver rr{a.block_table, SPARSE ? a.topk_length : a.cache_seqlens, a.indices, a.s_q, a.max_blocks,
+                   SPARSE ? a.topk : 0,
                    a.causal, a.num_rows};
 
     const int head = hblk * kHeadsPerWG + hb * 32 + l32;   // this lane's head
@@ -745,7 +746,10 @@ __global__ void __launch_bounds__(kThreads, 1) decode_kernel(const DecodeArgs a)
         const bool final_out = (nsplit == 1);
         const int b = j / a.s_q, iq = j - b * a.s_q;
         if (final_out || (slot >= 0 && slot < a.max_slots)) {
-            const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
+            const float lse_v = l_run > 0.f ? (c * m_run + log2f(l_run)) * 0.69314718055994531f : -INFINITY;
+            float inv = l_run > 0.f ? 1.f / l_run : 0.f;
+            // attention sink: a final output is scaled by exp(lse) / (exp(lse) + exp(sink))
+            if (final_out && a.attn_sink && head_ok) inv *= 1.f / (1.f + __expf(a.attn_sink[head] - lse_v));
             if (head_ok) {
 #pragma unroll
                 for (int dd = 0; dd < 8; ++dd) {
@@ -770,7 +774,6 @@ __global__ void __launch_bounds__(kThreads, 1) decode_kernel(const DecodeArgs a)
                 }
             }
             if (kh == 0 && lane < 32 && head_ok) {
-                const float lse_v = l_run > 0.f ? (c * m_run + log2f(l_run)) * 0.69314718055994531f : -INFINITY;
                 if (final_out) a.lse[((int64_t)b * H + head) * a.s_q + iq] = lse_v;
                 else a.lse_part[(int64_t)slot * H + head] = lse_v;
             }

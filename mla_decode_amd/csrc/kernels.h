@@ -12,6 +12,8 @@ struct DecodeArgs {
     const int32_t* block_table;  // dense
     const int32_t* cache_seqlens;
     const int32_t* indices;      // sparse
+    const int32_t* topk_length;  // sparse: [B*S] top-k entries used per query token, or null (all)
+    const float* attn_sink;      // [H] per-head sink logits, or null
     const int32_t* meta;         // scheduler metadata (device)
     float* o_part;               // [max_slots, H, 512]
     float* lse_part;             // [max_slots, H]
@@ -25,7 +27,7 @@ struct DecodeArgs {
 };
 
 struct MetaArgs {
-    const int32_t* cache_seqlens;
+    const int32_t* cache_seqlens;   // dense: [batch]; sparse: topk_length [batch*s_q] or null
     int32_t* meta;
     int batch, s_q, max_blocks, topk, causal, num_parts, fixed_overhead;
 };
@@ -34,6 +36,7 @@ struct CombineArgs {
     const float* o_part;
     const float* lse_part;
     const int32_t* split_offsets;
+    const float* attn_sink;      // [H] or null
     void* out;
     float* lse;
     int num_items, h_q, s_q, out_fp32, skip_single;
@@ -41,7 +44,7 @@ struct CombineArgs {
 
 struct GatherArgs {
     const int32_t* table_or_indices;
-    const int32_t* cache_seqlens;
+    const int32_t* cache_seqlens;   // dense: [batch]; sparse: topk_length [batch*s_q] or null
     int32_t* rows_out;
     int64_t num_rows;
     int batch, s_q, max_blocks, topk, causal, row_stride;

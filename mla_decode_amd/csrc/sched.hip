@@ -1,7 +1,8 @@
 // Split-KV tile scheduler, one workgroup, integer arithmetic only.
 //
 // Items are query tokens (j = b*s_q + i) with n_j KV tiles of 64 tokens
-// (dense: causal-visible length; sparse: topk).  Each item costs n_j + F;
+// (dense: causal-visible length; sparse: topk, or the item's top-k length
+// clamped to [0, topk]).  Each item costs n_j + F;
 // the prefix sum C_j of the costs is cut into P equal runs of q = ceil(T/P)
 // cost units and every partition records the (item, tile) range it covers.
 // The first F cost units of an item carry no tile: they stand for the item's
@@ -51,7 +52,7 @@ __global__ void __launch_bounds__(kSchedThreads) metadata_kernel(const MetaArgs 
     const int tid = threadIdx.x;
 
     auto tiles_of = [&](int j) -> int {
-        if (a.topk > 0) return (a.topk + 63) >> 6;
+        if (a.topk > 0) return ((a.cache_seqlens ? topk_slots(a.cache_seqlens[j], a.topk) : a.topk) + 63) >> 6;
         const int b = j / a.s_q, i = j - b * a.s_q;
         return (visible_len(clamp_len(a.cache_seqlens[b], a.max_blocks), a.s_q, i, a.causal) + 63) >> 6;
     };

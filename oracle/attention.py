@@ -22,6 +22,10 @@ What is computed (sources, by page title and section):
   offset, -1 marks an invalid entry and block_table is not used; the kernel
   returns out [b, s_q, h_q, d_v] and lse [b, h_q, s_q] in float32 (transposed
   with respect to out).
+* Same README, sparse attention arguments: an optional per-head
+  ``attn_sink`` scales the output by exp(lse) / (exp(lse) + exp(attn_sink)),
+  and an optional ``topk_length`` restricts a query token to the first
+  topk_length entries of its index row.
 
 Readings where the pages are silent (each also listed in the design notes):
 * scores are multiplied by ``softmax_scale``; lse is the natural-log
@@ -31,7 +35,10 @@ Readings where the pages are silent (each also listed in the design notes):
 * a query that sees no token gets out = 0 and lse = -inf;
 * a top-k index < 0 or >= num_blocks*block_size is treated as invalid
   (the pages say only -1 is invalid and that no upper-bound check is made);
-* duplicate top-k entries each count (the slot multiset).
+* duplicate top-k entries each count (the slot multiset);
+* ``topk_length`` is given per decode query token ([b, s_q]; the README's
+  prefill call gives it per query row) and clamped to [0, topk]; lse is not
+  changed by the sink.
 
 Everything is float64 on the exact values of the bfloat16 (or dequantised
 FP8) inputs, so the result is the mathematical value up to float64 rounding.
@@ -171,10 +178,23 @@ def paged_rows(block_table_row, n):
     return np.asarray(block_table_row, dtype=np.int64)[t // BLOCK] * BLOCK + t % BLOCK
 
 
-def sparse_rows(index_row, num_rows):
-    """Valid physical rows of one top-k index row (the slot multiset)."""
+def sparse_rows(index_row, num_rows, length=None):
+    """Valid physical rows of one top-k index row (the slot multiset), over
+    its first ``length`` entries when a top-k length is given."""
     idx = np.asarray(index_row, dtype=np.int64)
+    if length is not None:
+        idx = idx[:min(max(int(length), 0), idx.shape[0])]
     return idx[(idx >= 0) & (idx < num_rows)]
+
+
+def apply_sink(out, lse, sink):
+    """Scale one query group's rows by exp(lse) / (exp(lse) + exp(sink)) per
+    head; lse unchanged.  A row that sees nothing (lse = -inf) stays 0."""
+    sink = np.asarray(sink, dtype=np.float64)
+    f = np.zeros_like(lse)
+    ok = np.isfinite(lse)
+    f[ok] = 1.0 / (1.0 + np.exp(sink[ok] - lse[ok]))
+    return out * f[:, None]
 
 
 def gather_rows_dense(block_table, cache_seqlens, s_q, causal):
@@ -190,13 +210,15 @@ def gather_rows_dense(block_table, cache_seqlens, s_q, causal):
 # whole-batch decode
 
 def decode(q_bits, kv, softmax_scale, *, block_table=None, cache_seqlens=None,
-           indices=None, causal=False, kv_format='bf16', items=None):
+           indices=None, causal=False, kv_format='bf16', items=None, topk_length=None, attn_sink=None):
     """Absorbed-MLA decode over a batch, float64.
 
     q_bits   uint16 [B, S, H, 576]   bfloat16 bit patterns of the absorbed q
     kv       uint16 [R, 576] (bf16) or uint8 [R, 656] (fp8), R = num_blocks*64
     dense:   block_table int [B, max_blocks], cache_seqlens int [B]
-    sparse:  indices int [B, S, topk]  (block_table unused)
+    sparse:  indices int [B, S, topk]  (block_table unused); topk_length
+             optional int [B, S]
+    attn_sink optional float [H]
     items    optional list of (b, i) to compute; default all
 
     Returns out float64 [B, S, H, 512] and lse float64 [B, H, S]; entries not
@@ -212,13 +234,15 @@ def decode(q_bits, kv, softmax_scale, *, block_table=None, cache_seqlens=None,
         items = [(b, i) for b in range(B) for i in range(S)]
     for (b, i) in items:
         if indices is not None:
-            rows = sparse_rows(indices[b, i], num_rows)
+            rows = sparse_rows(indices[b, i], num_rows, None if topk_length is None else topk_length[b][i])
         else:
             L = int(cache_seqlens[b])
             rows = paged_rows(block_table[b], visible_len(L, S, i, causal))
         Kf = kv_values(kv, rows, kv_format)
         qh = bf16_bits_to_f64(q_bits[b, i])
         o, ls = attend(qh, Kf, Kf[:, :D_V], softmax_scale)
+        if attn_sink is not None:
+            o = apply_sink(o, ls, attn_sink)
         out[b, i] = o
         lse[b, :, i] = ls
     return out, lse

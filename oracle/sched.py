@@ -75,8 +75,14 @@ def item_tiles_dense(cache_seqlens, s_q, causal):
     return np.asarray(out, dtype=np.int64)
 
 
-def item_tiles_sparse(batch, s_q, topk):
-    return np.full(batch * s_q, (int(topk) + BLOCK - 1) // BLOCK, dtype=np.int64)
+def item_tiles_sparse(batch, s_q, topk, topk_length=None):
+    """Tiles per item of a top-k problem: all topk entries, or each query
+    token's top-k length clamped to [0, topk]."""
+    if topk_length is None:
+        return np.full(batch * s_q, (int(topk) + BLOCK - 1) // BLOCK, dtype=np.int64)
+    n = np.clip(np.asarray(topk_length, dtype=np.int64).reshape(-1), 0, int(topk))
+    assert n.shape[0] == batch * s_q
+    return (n + BLOCK - 1) // BLOCK
 
 
 def schedule(n, P, F):

@@ -54,11 +54,14 @@ def run_library(w, num_cus=0, stream=None, rescale_threshold=0.0):
 def oracle(w, items=None, kv=None):
     q = bits16(w.q)
     kv = kv_host(w) if kv is None else kv
+    sink = None if getattr(w, "attn_sink", None) is None else w.attn_sink.cpu().double().numpy()
     if w.topk:
-        return A.decode(q, kv, w.softmax_scale, indices=w.indices.cpu().numpy(), kv_format=w.kv_format, items=items)
+        tl = None if getattr(w, "topk_length", None) is None else w.topk_length.cpu().numpy()
+        return A.decode(q, kv, w.softmax_scale, indices=w.indices.cpu().numpy(), kv_format=w.kv_format, items=items,
+                        topk_length=tl, attn_sink=sink)
     return A.decode(q, kv, w.softmax_scale, block_table=w.block_table.cpu().numpy(),
                     cache_seqlens=w.cache_seqlens.cpu().numpy(), causal=w.causal, kv_format=w.kv_format,
-                    items=items)
+                    items=items, attn_sink=sink)
 
 
 def compare(got_out, got_lse, ref_out, ref_lse, items=None, rel_l2=OUT_REL_L2, max_abs=OUT_MAX_ABS, lse_abs=LSE_ABS):

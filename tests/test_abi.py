@@ -107,23 +107,23 @@ def test_decode_rejects_bad_arguments_before_launch(lib):
     ws = mla.workspace_bytes(m)
     fake = ctypes.c_void_p(1 << 20)       # never dereferenced: validation fails first
     # metadata has no device buffer
-    assert lib.mla_decode_fwd(ctypes.byref(p), fake, fake, fake, fake, ctypes.byref(m), fake, ws, fake, fake,
+    assert lib.mla_decode_fwd(ctypes.byref(p), fake, fake, fake, fake, None, ctypes.byref(m), fake, ws, fake, fake,
                               None) == 1
     m.dev = 1 << 20
     # workspace too small
-    assert lib.mla_decode_fwd(ctypes.byref(p), fake, fake, fake, fake, ctypes.byref(m), fake, ws - 1, fake, fake,
-                              None) == 3
+    assert lib.mla_decode_fwd(ctypes.byref(p), fake, fake, fake, fake, None, ctypes.byref(m), fake, ws - 1, fake,
+                              fake, None) == 3
     # misaligned q
-    assert lib.mla_decode_fwd(ctypes.byref(p), ctypes.c_void_p((1 << 20) + 2), fake, fake, fake,
+    assert lib.mla_decode_fwd(ctypes.byref(p), ctypes.c_void_p((1 << 20) + 2), fake, fake, fake, None,
                               ctypes.byref(m), fake, ws, fake, fake, None) == 1
     # metadata planned for another problem
     p2 = _problem(batch=32)
-    assert lib.mla_decode_fwd(ctypes.byref(p2), fake, fake, fake, fake, ctypes.byref(m), fake, ws, fake, fake,
+    assert lib.mla_decode_fwd(ctypes.byref(p2), fake, fake, fake, fake, None, ctypes.byref(m), fake, ws, fake, fake,
                               None) == 4
     # sparse entry point on a dense problem
-    assert lib.mla_sparse_decode_fwd(ctypes.byref(p), fake, fake, fake, ctypes.byref(m), fake, ws, fake, fake,
-                                     None) == 1
+    assert lib.mla_sparse_decode_fwd(ctypes.byref(p), fake, fake, fake, None, None, ctypes.byref(m), fake, ws, fake,
+                                     fake, None) == 1
     # combine argument checks
-    assert lib.mla_combine(0, 128, 1, fake, fake, fake, 0, fake, fake, None) == 1
-    assert lib.mla_combine(3, 128, 2, fake, fake, fake, 0, fake, fake, None) == 1
-    assert lib.mla_combine(4, 128, 2, fake, fake, fake, 7, fake, fake, None) == 1
+    assert lib.mla_combine(0, 128, 1, fake, fake, fake, None, 0, fake, fake, None) == 1
+    assert lib.mla_combine(3, 128, 2, fake, fake, fake, None, 0, fake, fake, None) == 1
+    assert lib.mla_combine(4, 128, 2, fake, fake, fake, None, 7, fake, fake, None) == 1

@@ -281,3 +281,72 @@ def test_peaked_rows_are_self_dominated():
         weights.extend(p[:, 0].tolist())
     med = float(np.median(weights))
     assert 0.08 < med < 0.3
+
+
+# ------------------------------------------------------------------ optional arguments: attn_sink, topk_length
+
+def test_sink_is_a_zero_value_token():
+    """The sink scaling exp(lse) / (exp(lse) + exp(sink)) equals attention with
+    one extra key whose scaled score is the sink and whose value is 0 (an
+    independent form of the same softmax); lse stays the sink-free one, and
+    the extra-key lse is logaddexp(lse, sink)."""
+    w = make_dense(2, 1, 6, [70, 9], seed=31, max_blocks=2)
+    q = _bits(w.q)
+    kv = _bits(w.kv).reshape(-1, 576)
+    bt, sl = w.block_table.numpy(), w.cache_seqlens.numpy()
+    sink = np.array([-3.0, 0.0, 1.5, 4.0, 9.0, -np.inf])
+    out, lse = A.decode(q, kv, w.softmax_scale, block_table=bt, cache_seqlens=sl)
+    outs, lses = A.decode(q, kv, w.softmax_scale, block_table=bt, cache_seqlens=sl, attn_sink=sink)
+    assert np.array_equal(lses, lse)
+    fin = np.isfinite(sink)
+    for b in range(2):
+        qh = bf16_bits_to_f64(q[b, 0])
+        K = A.kv_values(kv, A.paged_rows(bt[b], int(sl[b])), 'bf16')
+        # extra key k with scale * qh[h] . k = sink[h] for the finite sinks (least-norm solution)
+        Qf = qh[fin]
+        k = Qf.T @ np.linalg.solve(Qf @ Qf.T, sink[fin] / w.softmax_scale)
+        assert np.max(np.abs(w.softmax_scale * Qf @ k - sink[fin])) < 1e-9
+        o2, l2 = A.attend(qh, np.vstack([K, k]), np.vstack([K[:, :512], np.zeros((1, 512))]), w.softmax_scale)
+        assert np.max(np.abs(outs[b, 0][fin] - o2[fin])) < 1e-10
+        assert np.max(np.abs(l2[fin] - np.logaddexp(lse[b, fin, 0], sink[fin]))) < 1e-9
+        # sink = -inf leaves the row exactly as without a sink
+        assert np.array_equal(outs[b, 0][~fin], out[b, 0][~fin])
+
+
+def test_sink_equal_to_lse_halves_the_output():
+    w = make_dense(1, 1, 4, [100], seed=32, max_blocks=2)
+    q = _bits(w.q)
+    kv = _bits(w.kv).reshape(-1, 576)
+    args = dict(block_table=w.block_table.numpy(), cache_seqlens=w.cache_seqlens.numpy())
+    out, lse = A.decode(q, kv, w.softmax_scale, **args)
+    outs, _ = A.decode(q, kv, w.softmax_scale, attn_sink=lse[0, :, 0], **args)
+    assert np.max(np.abs(outs - 0.5 * out)) <= 1e-15 * np.max(np.abs(out))
+
+
+def test_sink_on_an_empty_row():
+    w = make_dense(1, 1, 4, [0], seed=33, max_blocks=1)
+    out, lse = A.decode(_bits(w.q), _bits(w.kv).reshape(-1, 576), w.softmax_scale,
+                        block_table=w.block_table.numpy(), cache_seqlens=w.cache_seqlens.numpy(),
+                        attn_sink=np.array([0.0, 5.0, -5.0, -np.inf]))
+    assert np.all(out == 0) and np.all(np.isneginf(lse))
+
+
+def test_topk_length_equals_masking_the_tail():
+    """A query token's top-k length L gives the same result as marking its
+    entries from L on invalid (-1); L >= topk is the whole row, L <= 0 sees
+    nothing."""
+    w = make_sparse(2, 2, 4, pool_tokens_per_seq=256, topk=50, invalid_frac=0.1, seed=34)
+    q = _bits(w.q)
+    kv = _bits(w.kv).reshape(-1, 576)
+    idx = w.indices.numpy()
+    lengths = np.array([[17, 0], [50, 99]])
+    out, lse = A.decode(q, kv, w.softmax_scale, indices=idx, topk_length=lengths)
+    masked = idx.copy()
+    for b in range(2):
+        for i in range(2):
+            masked[b, i, max(lengths[b, i], 0):] = -1
+    out2, lse2 = A.decode(q, kv, w.softmax_scale, indices=masked)
+    assert np.array_equal(out, out2) and np.array_equal(lse, lse2)
+    full, lfull = A.decode(q, kv, w.softmax_scale, indices=idx)
+    assert np.array_equal(out[1, 0], full[1, 0]) and np.array_equal(out[1, 1], full[1, 1])
+    assert np.all(out[0, 1] == 0) and np.all(np.isneginf(lse[0, :, 1]))

@@ -108,3 +108,15 @@ def test_sparse_whole_item_rule():
         n = S.item_tiles_sparse(128, 2, topk)
         sch = S.schedule(n, 256, 0)
         assert sch['q'] % int(n[0]) == 0 and (sch['num_splits'] == 1).all()
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_sparse_topk_lengths(seed):
+    """Per-query top-k lengths (clamped to [0, topk]) through the same
+    brute-force check as dense lengths."""
+    rng = np.random.default_rng(100 + seed)
+    batch, s_q, topk = int(rng.integers(1, 5)), int(rng.integers(1, 3)), int(rng.integers(1, 300))
+    lengths = rng.integers(-5, topk + 80, size=(batch, s_q))
+    n = S.item_tiles_sparse(batch, s_q, topk, lengths)
+    assert n.tolist() == [(min(max(int(x), 0), topk) + 63) // 64 for x in lengths.reshape(-1)]
+    check(n.tolist(), int(rng.integers(1, 9)), int(rng.integers(0, 3)))

@@ -57,6 +57,8 @@ class Workload:
     cache_seqlens: torch.Tensor     # int32 [B]
     indices: Optional[torch.Tensor] = None   # int32 [B, S, topk]
     meta: dict = field(default_factory=dict)
+    topk_length: Optional[torch.Tensor] = None   # int32 [B, S] or None (all topk entries)
+    attn_sink: Optional[torch.Tensor] = None     # float32 [H] or None
 
     @property
     def num_blocks(self):
@@ -68,7 +70,7 @@ class Workload:
 
     def to(self, device):
         kw = {}
-        for k in ('q', 'kv', 'block_table', 'cache_seqlens', 'indices'):
+        for k in ('q', 'kv', 'block_table', 'cache_seqlens', 'indices', 'topk_length', 'attn_sink'):
             v = getattr(self, k)
             kw[k] = None if v is None else v.to(device)
         return Workload(self.name, self.batch, self.s_q, self.h_q, self.causal, self.topk,
