@@ -9,7 +9,10 @@ a 4096-page pool, bf16 N(0,1) inputs, inputs resident in HBM).
 ``--workload fp8_sparse_topk2048`` / ``fp8_sparse_topk32768`` time instead
 the FP8 sparse decode shape the pages quote for their H800 kernel (b=128,
 s_q=2, h_q=128, top-k 2048 or 32768 over 656-byte records,
-mla_sparse_decode_fwd); that line's roofline is the MFMA one.
+mla_sparse_decode_fwd); ``--workload sparse_prefill`` times the top-k sparse
+prefill (mla_sparse_prefill_fwd) of 4096 query rows at the end of a
+32768-row bf16 cache, top-k 2048, 128 heads.  Those lines' roofline is the
+MFMA one.
 
 Prints one JSON line.  ``value`` is TFLOP/s of algorithmic work (FLOPs =
 2 h_q (576 + 512) per visible query-token/KV-token pair) per step; the line
@@ -71,7 +74,8 @@ def cpu_baseline_sparse(w):
     for b in range(w.batch):
         for i in range(w.s_q):
             rows = idx[b, i][(idx[b, i] >= 0) & (idx[b, i] < nrows)]
-            kv = kv_rows[torch.from_numpy(rows.astype(np.int64)).to(w.kv.device)].cpu().numpy()   # gathered on the GPU
+            got = kv_rows[torch.from_numpy(rows.astype(np.int64)).to(w.kv.device)].cpu()   # gathered on the GPU
+            kv = got.numpy() if w.kv_format == "fp8" else got.view(torch.int16).numpy().view(np.uint16)
             t0 = time.perf_counter()
             A.decode_partial(q, kv, w.softmax_scale, np.arange(len(rows)), b, i, kv_format=w.kv_format)
             dt += time.perf_counter() - t0
@@ -109,6 +113,65 @@ def cpu_baseline(w, flops):
                       f"fp64 numpy, {dt:.1f} s in total"}
 
 
+def _timed(fn, steps, stream):
+    import torch
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(steps):
+        fn()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps
+
+
+def bench_prefill(args):
+    """Top-k sparse prefill: 4096 query rows, the last of a 32768-row bf16 cache, top-k 2048, 128 heads."""
+    import types
+    import torch
+    import mla_decode_amd as mla
+    from workloads import make_sparse_prefill
+    dev = torch.device("cuda:0")
+    s_q, s_kv, h_q, topk = 4096, 32768, 128, 2048
+    w = make_sparse_prefill(s_q, s_kv, h_q, topk, seed=3000, device=dev)
+    p = mla.make_problem(1, s_q, h_q, s_kv // 64, topk=topk, softmax_scale=w.softmax_scale)
+    dec = mla.Decoder(p, dev)
+    stream = torch.cuda.current_stream(dev)
+    valid = int(((w.indices >= 0) & (w.indices < s_kv)).sum())
+    flops = 2.0 * h_q * (576 + 512) * valid
+    nbytes = float(s_q * h_q * 1152 + s_kv * 1152 + s_q * h_q * (1024 + 4) + w.indices.numel() * 4)
+
+    def step():
+        dec.metadata(None, stream)
+        mla.sparse_prefill_fwd(p, s_kv, w.q, w.kv, w.indices, dec.meta, dec.workspace, dec.out, dec.lse, stream)
+
+    for _ in range(args.warmup):
+        step()
+    ms_step = _timed(step, args.steps, stream)
+    ms_kernel = _timed(lambda: dec.decode_partial(w.q, w.kv, None, None, w.indices, stream), args.steps, stream)
+    kern_tflops = flops / (ms_kernel * 1e-3) / 1e12
+    line = {
+        "metric": "MLA sparse prefill TFLOPS, µs/step at s_q=4096,s_kv=32768,h_q=128,topk=2048 (1 GPU)",
+        "value": round(flops / (ms_step * 1e-3) / 1e12, 2), "unit": "TFLOPS", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_step, 5), "us_per_step": round(ms_step * 1e3, 2),
+        "hbm_gbs": round(nbytes / (ms_step * 1e-3) / 1e9, 1), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "top-k sparse prefill: 4096 query rows at the end of a 32768-row flat bf16 cache, "
+                               "top-k 2048 of each row's visible rows, 128 heads, N(0,1) inputs",
+                   "s_q": s_q, "s_kv": s_kv, "h_q": h_q, "topk": topk, "d_qk": 576, "d_v": 512,
+                   "step": "metadata + sparse prefill (partial + combine when needed)"},
+        "roofline": {"bound": "mfma", "kernel": "decode_kernel<sparse, bf16 cache> (partial attention)",
+                     "achieved": round(kern_tflops, 1), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(kern_tflops / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
+                     "algorithmic_flops": flops, "us_per_launch": round(ms_kernel * 1e3, 2)},
+    }
+    if not args.no_cpu_baseline:
+        view = types.SimpleNamespace(batch=1, s_q=s_q, h_q=h_q, topk=topk, kv=w.kv, kv_format="bf16",
+                                     q=w.q[None], indices=w.indices[:, 0, :][None], softmax_scale=w.softmax_scale)
+        line["cpu_baseline"] = cpu_baseline_sparse(view)
+    print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -116,7 +179,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--workload", default="dense_b64_s4096",
-                    choices=["dense_b64_s4096", "fp8_sparse_topk2048", "fp8_sparse_topk32768"],
+                    choices=["dense_b64_s4096", "fp8_sparse_topk2048", "fp8_sparse_topk32768", "sparse_prefill"],
                     help="dense_b64_s4096 is the headline line; the others time the pages' FP8 sparse shape")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a 1 GiB device copy 5 times (reference for HBM byte counters)")
@@ -139,6 +202,9 @@ def main():
     import torch
     import mla_decode_amd as mla
     from workloads import make_config, make_fp8_sparse, flops_and_bytes
+
+    if args.workload == "sparse_prefill":
+        return bench_prefill(args)
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = torch.device("cuda:0")

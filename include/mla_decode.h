@@ -178,6 +178,24 @@ mla_status_t mla_sparse_decode_fwd(const mla_problem_t *problem, const void *q, 
                                    const mla_metadata_t *meta, void *workspace, size_t workspace_bytes,
                                    void *out, float *lse, void *stream);
 
+/* Top-k sparse prefill (README copy, "DSA Prefill", flash_mla_sparse_fwd):
+ * every query row s of q [s_q, h_q, 576] attends to the rows
+ * indices[s, 0, :] (device int32 [s_q, 1, topk]; entries < 0 or >= s_kv are
+ * invalid) of a flat, unpaged cache kv [s_kv, 1, 576] bfloat16 (or
+ * [s_kv, 1, 656] FP8 records), writing out [s_q, h_q, 512] and lse
+ * [h_q, s_q].  It is the sparse decode of one request with s_q query tokens:
+ * ``problem`` has batch = 1, s_q = the number of query rows (at most 16384
+ * per call), topk > 0, causal 0 and num_blocks >= ceil(s_kv / 64); plan and
+ * metadata are made as for mla_sparse_decode_fwd; topk_length ([s_q]) and
+ * attn_sink ([h_q]) are optional.  The README copy gives this call on the
+ * 512-wide head of its newer model; here it serves the 576-wide latent head
+ * of the decode path.  Errors: as mla_sparse_decode_fwd, plus INVALID_ARG
+ * when batch != 1 or s_kv is not in [1, num_blocks*64]. */
+mla_status_t mla_sparse_prefill_fwd(const mla_problem_t *problem, int32_t s_kv, const void *q, const void *kv,
+                                    const int32_t *indices, const int32_t *topk_length, const float *attn_sink,
+                                    const mla_metadata_t *meta, void *workspace, size_t workspace_bytes,
+                                    void *out, float *lse, void *stream);
+
 /* LSE merge of split partials ("matrices, attention & GPU" explainer,
  * split-KV section: m = max(m1, m2), l = l1 e^(m1-m) + l2 e^(m2-m),
  * o = (o1 l1 e^(m1-m) + o2 l2 e^(m2-m)) / l).  Item j = b*s_q + i owns the

@@ -17,7 +17,8 @@ from . import _lib
 from ._lib import MlaError, Problem, Metadata  # noqa: F401
 
 __all__ = ["make_problem", "plan", "workspace_bytes", "get_decode_metadata", "decode_fwd",
-           "sparse_decode_fwd", "combine", "debug_gather_rows", "Decoder", "MlaError", "abi_version"]
+           "sparse_decode_fwd", "sparse_prefill_fwd", "sparse_prefill", "combine", "debug_gather_rows", "Decoder",
+           "MlaError", "abi_version"]
 
 
 def _ptr(t):
@@ -141,6 +142,44 @@ def sparse_decode_fwd(problem, q, kv_cache, indices, meta, workspace, out, lse, 
         ctypes.byref(problem), _ptr(q), _ptr(kv_cache), _ptr(indices), _ptr(tl), _ptr(sink), ctypes.byref(meta),
         _ptr(workspace),
         workspace.numel() * workspace.element_size(), _ptr(out), _ptr(lse), _stream(stream)))
+
+
+def sparse_prefill_fwd(problem, s_kv, q, kv, indices, meta, workspace, out, lse, stream=None, topk_length=None,
+                       attn_sink=None):
+    """Top-k sparse prefill over a flat cache of s_kv rows (mla_sparse_prefill_fwd); ``problem`` has batch 1."""
+    lib = _lib.load()
+    _need(q, "q", torch.bfloat16)
+    _need(kv, "kv", None)
+    _need(indices, "indices", torch.int32)
+    _need(workspace, "workspace", None)
+    _need(out, "out", None)
+    _need(lse, "lse", torch.float32)
+    tl, sink = _topk_length(problem, topk_length), _attn_sink(problem.h_q, attn_sink)
+    _lib.check("mla_sparse_prefill_fwd", lib.mla_sparse_prefill_fwd(
+        ctypes.byref(problem), int(s_kv), _ptr(q), _ptr(kv), _ptr(indices), _ptr(tl), _ptr(sink),
+        ctypes.byref(meta), _ptr(workspace), workspace.numel() * workspace.element_size(), _ptr(out), _ptr(lse),
+        _stream(stream)))
+
+
+def sparse_prefill(q, kv, indices, sm_scale=None, topk_length=None, attn_sink=None, out_dtype="bf16", num_cus=0,
+                   rescale_threshold=0.0, stream=None):
+    """DSA sparse prefill in the README's argument order: q [s_q, h_q, 576], kv [s_kv, 1, 576] bfloat16 (or
+    [s_kv, 1, 656] FP8 records), indices [s_q, 1, topk] -> (out [s_q, h_q, 512], lse [h_q, s_q]).  Plans,
+    schedules and allocates the outputs and workspace with torch on q's device, then runs the library."""
+    s_q, h_q = int(q.shape[0]), int(q.shape[1])
+    s_kv, topk = int(kv.shape[0]), int(indices.shape[-1])
+    fmt = "fp8" if kv.dtype == torch.uint8 else "bf16"
+    p = make_problem(1, s_q, h_q, (s_kv + 63) // 64, topk=topk, kv_format=fmt, out_dtype=out_dtype,
+                     softmax_scale=sm_scale, rescale_threshold=rescale_threshold)
+    m = plan(p, num_cus)
+    dev = q.device
+    meta_buf = torch.zeros((m.bytes + 15) // 16 * 4, dtype=torch.int32, device=dev)
+    ws = torch.empty(max(16, (workspace_bytes(m) + 15) // 16 * 4), dtype=torch.float32, device=dev)
+    out = torch.empty((s_q, h_q, 512), dtype=torch.float32 if out_dtype == "fp32" else torch.bfloat16, device=dev)
+    lse = torch.empty((h_q, s_q), dtype=torch.float32, device=dev)
+    get_decode_metadata(p, None, m, meta_buf, stream, topk_length)
+    sparse_prefill_fwd(p, s_kv, q, kv, indices, m, ws, out, lse, stream, topk_length, attn_sink)
+    return out, lse
 
 
 def combine(num_items, h_q, s_q, o_part, lse_part, split_offsets, out, lse, stream=None, attn_sink=None):

@@ -20,7 +20,8 @@ OUT_BF16 = 0
 OUT_FP32 = 1
 
 EXPORTED = ("mla_abi_version", "mla_status_string", "mla_plan", "mla_workspace_bytes",
-            "mla_get_decode_metadata", "mla_decode_fwd", "mla_sparse_decode_fwd", "mla_combine",
+            "mla_get_decode_metadata", "mla_decode_fwd", "mla_sparse_decode_fwd", "mla_sparse_prefill_fwd",
+            "mla_combine",
             "mla_debug_gather_rows", "mla_debug_decode_partial")
 
 
@@ -75,6 +76,9 @@ def load():
     lib.mla_sparse_decode_fwd.restype = ctypes.c_int
     lib.mla_sparse_decode_fwd.argtypes = [P(Problem), vp, vp, vp, vp, vp, P(Metadata), vp, ctypes.c_size_t, vp, vp,
                                           vp]
+    lib.mla_sparse_prefill_fwd.restype = ctypes.c_int
+    lib.mla_sparse_prefill_fwd.argtypes = [P(Problem), i32, vp, vp, vp, vp, vp, P(Metadata), vp, ctypes.c_size_t,
+                                           vp, vp, vp]
     lib.mla_combine.restype = ctypes.c_int
     lib.mla_combine.argtypes = [i32, i32, i32, vp, vp, vp, vp, i32, vp, vp, vp]
     lib.mla_debug_gather_rows.restype = ctypes.c_int

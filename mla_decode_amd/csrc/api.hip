@@ -99,8 +99,9 @@ bool sparse_items_whole(const mla_problem_t* p, const mla_metadata_t* m) {
 
 mla_status_t run_decode(const mla_problem_t* p, bool sparse, const void* q, const void* kv,
                         const int32_t* block_table, const int32_t* cache_seqlens, const int32_t* indices,
-                        const int32_t* topk_length, const float* attn_sink, const mla_metadata_t* meta, void* ws, size_t ws_bytes, void* out, float* lse,
-                        void* stream, bool run_combine = true) {
+                        const int32_t* topk_length, const float* attn_sink, const mla_metadata_t* meta,
+                        void* ws, size_t ws_bytes, void* out, float* lse, void* stream, bool run_combine = true,
+                        int64_t num_rows = 0) {
     mla_status_t st = validate(p);
     if (st != MLA_OK) return st;
     if (sparse != (p->topk > 0)) return MLA_ERR_INVALID_ARG;
@@ -127,7 +128,7 @@ mla_status_t run_decode(const mla_problem_t* p, bool sparse, const void* q, cons
     a.lse_part = (float*)ws + slots * p->h_q * mla::kDv;
     a.out = out;
     a.lse = lse;
-    a.num_rows = (int64_t)p->num_blocks * kBlock;
+    a.num_rows = num_rows > 0 ? num_rows : (int64_t)p->num_blocks * kBlock;   // rows a valid index may name
     a.batch = p->batch;
     a.s_q = p->s_q;
     a.h_q = p->h_q;
@@ -239,6 +240,16 @@ mla_status_t mla_sparse_decode_fwd(const mla_problem_t* problem, const void* q, 
                                    float* lse, void* stream) {
     return run_decode(problem, true, q, kv_cache, nullptr, nullptr, indices, topk_length, attn_sink, meta,
                       workspace, workspace_bytes, out, lse, stream);
+}
+
+mla_status_t mla_sparse_prefill_fwd(const mla_problem_t* problem, int32_t s_kv, const void* q, const void* kv,
+                                    const int32_t* indices, const int32_t* topk_length, const float* attn_sink,
+                                    const mla_metadata_t* meta, void* workspace, size_t workspace_bytes, void* out,
+                                    float* lse, void* stream) {
+    if (!problem || problem->batch != 1 || problem->topk < 1) return MLA_ERR_INVALID_ARG;
+    if (s_kv < 1 || (int64_t)s_kv > (int64_t)problem->num_blocks * kBlock) return MLA_ERR_INVALID_ARG;
+    return run_decode(problem, true, q, kv, nullptr, nullptr, indices, topk_length, attn_sink, meta, workspace,
+                      workspace_bytes, out, lse, stream, true, s_kv);
 }
 
 mla_status_t mla_combine(int32_t num_items, int32_t h_q, int32_t s_q, const float* o_part, const float* lse_part,

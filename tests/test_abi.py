@@ -127,3 +127,20 @@ def test_decode_rejects_bad_arguments_before_launch(lib):
     assert lib.mla_combine(0, 128, 1, fake, fake, fake, None, 0, fake, fake, None) == 1
     assert lib.mla_combine(3, 128, 2, fake, fake, fake, None, 0, fake, fake, None) == 1
     assert lib.mla_combine(4, 128, 2, fake, fake, fake, None, 7, fake, fake, None) == 1
+
+
+def test_prefill_rejects_bad_arguments_before_launch(lib):
+    import mla_decode_amd as mla
+    fake = ctypes.c_void_p(1 << 20)       # never dereferenced: validation fails first
+    p = mla.make_problem(1, 300, 128, 16, topk=600)
+    m = mla.plan(p, num_cus=256)
+    m.dev = 1 << 20
+    ws = mla.workspace_bytes(m)
+    call = lambda prob, s_kv: lib.mla_sparse_prefill_fwd(ctypes.byref(prob), s_kv, fake, fake, fake, None, None,
+                                                         ctypes.byref(m), fake, ws, fake, fake, None)
+    assert call(p, 0) == 1                 # empty cache
+    assert call(p, 16 * 64 + 1) == 1       # more rows than num_blocks*64
+    p2 = mla.make_problem(2, 150, 128, 16, topk=600)
+    assert call(p2, 1000) == 1             # prefill is one sequence
+    p3 = mla.make_problem(1, 300, 128, 16, max_blocks_per_seq=16)
+    assert call(p3, 1000) == 1             # dense problem

@@ -229,6 +229,50 @@ def make_fp8_sparse(topk, device='cpu', seed=None, batch=128, s_q=2, h_q=128):
                        device=device, kv_format='fp8', name=f'fp8_sparse_b{batch}_s{s_q}_topk{topk}')
 
 
+@dataclass
+class PrefillWorkload:
+    """Sparse prefill inputs: a flat, unpaged cache of s_kv rows."""
+    name: str
+    s_q: int
+    h_q: int
+    topk: int
+    kv_format: str                  # 'bf16' | 'fp8'
+    softmax_scale: float
+    q: torch.Tensor                 # bf16 [s_q, h_q, 576]
+    kv: torch.Tensor                # bf16 [s_kv, 1, 576] or uint8 [s_kv, 1, 656]
+    indices: torch.Tensor           # int32 [s_q, 1, topk]
+    topk_length: Optional[torch.Tensor] = None   # int32 [s_q]
+    attn_sink: Optional[torch.Tensor] = None     # float32 [h_q]
+
+    @property
+    def s_kv(self):
+        return int(self.kv.shape[0])
+
+
+def make_sparse_prefill(s_q, s_kv, h_q, topk, *, invalid_frac=0.0, seed=0, device='cpu', kv_format='bf16',
+                        name='sparse_prefill'):
+    """Query row s picks ``topk`` distinct rows of the first min(s_kv, s_kv - s_q + 1 + s) cache rows (the
+    rows a causal prefill chunk at the end of the sequence can see), each entry -1 with probability
+    ``invalid_frac``; q and cache values as for decode."""
+    g_cpu = _gen('cpu', seed)
+    idx = torch.empty((s_q, 1, topk), dtype=torch.int64)
+    for s in range(s_q):
+        vis = min(s_kv, s_kv - s_q + 1 + s)
+        assert vis >= topk
+        idx[s, 0] = torch.randperm(vis, generator=g_cpu)[:topk]
+    drop = torch.rand((s_q, 1, topk), generator=g_cpu) < invalid_frac
+    idx = torch.where(drop, torch.full_like(idx, -1), idx)
+    g = _gen(device, seed + 7919)
+    if kv_format == 'bf16':
+        kv = _randn_bf16((s_kv, 1, D_QK), g, device, chunk_rows=4096)
+    else:
+        x = torch.randn((s_kv, D_QK), generator=g, device=device)
+        kv = encode_fp8_records(x[:, :512].contiguous(), x[:, 512:].to(torch.bfloat16)).view(s_kv, 1, FP8_RECORD)
+    q = _randn_bf16((s_q, h_q, D_QK), g, device, chunk_rows=64)
+    return PrefillWorkload(name, s_q, h_q, topk, kv_format, 1.0 / math.sqrt(D_QK), q, kv,
+                           idx.to(torch.int32).to(device))
+
+
 def make_config(i, device='cpu', seed=None, **kw):
     """The five workloads, with seed 1000 + i unless given."""
     seed = 1000 + i if seed is None else seed
