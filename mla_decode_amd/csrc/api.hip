@@ -54,10 +54,6 @@ mla_status_t validate(const mla_problem_t* p) {
     const int64_t tiles = p->topk > 0 ? ((int64_t)p->topk + 63) / 64 : (int64_t)p->max_blocks_per_seq;
     if (items * (tiles + kFixedOverhead) >= ((int64_t)1 << 31)) return MLA_ERR_UNSUPPORTED;
     if ((int64_t)p->num_blocks * kBlock >= ((int64_t)1 << 31)) return MLA_ERR_UNSUPPORTED;
-    // the sparse bf16 gather addresses rows with 32-bit buffer offsets
-    if (p->topk > 0 && p->kv_format == MLA_KV_BF16_576 &&
-        (int64_t)p->num_blocks * kBlock * mla::kRowBytes >= ((int64_t)1 << 32))
-        return MLA_ERR_UNSUPPORTED;
     if ((int64_t)items * p->h_q * mla::kDv >= ((int64_t)1 << 40)) return MLA_ERR_UNSUPPORTED;
     return MLA_OK;
 }

@@ -114,11 +114,25 @@ __device__ __forceinline__ void dma_raw_x4(const i32x4& rs, int voff, int lds) {
     __asm__ volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen offset:%3 lds"
                      :: "s"(lds - IMM), "v"(voff), "s"(rs), "i"(IMM) : "memory", "m0");
 }
+
+// Gathered (sparse) rows are copied with a 64-bit address per lane, so caches
+// beyond 4 GiB are reached (a buffer offset is 32-bit).  As for the buffer
+// copies, the immediate offset moves both the source and the LDS destination
+// (LDS address = M0 + offset + 16 * lane for x4, 4 * lane for x1).  An invalid
+// row reads the zero row below instead, so it lands as zeros like an
+// out-of-range buffer load.
+__device__ __align__(16) unsigned char g_zero_row[kRowBytes];   // never written
 template <int IMM>
-__device__ __forceinline__ void dma_struct_x4(const i32x4& rs, int row, int voff, int lds) {
-    const i32x2 va = {row, voff};
-    __asm__ volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 idxen offen offset:%3 lds"
-                     :: "s"(lds - IMM), "v"(va), "s"(rs), "i"(IMM) : "memory", "m0");
+__device__ __forceinline__ void dma_global_x4(const unsigned char* src, int lds) {
+    __asm__ volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off offset:%2"
+                     :: "s"(lds - IMM), "v"(src), "i"(IMM) : "memory", "m0");
+}
+__device__ __forceinline__ void dma_global_x1(const unsigned char* src, int lds) {
+    __asm__ volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, off"
+                     :: "s"(lds), "v"(src) : "memory", "m0");
+}
+__device__ __forceinline__ const unsigned char* bf16_row_addr(const unsigned char* kv, int row, int off) {
+    return (row >= 0 ? kv + (int64_t)row * kRowBytes : g_zero_row) + off;
 }
 
 // ---- bf16 tile fill: 36 pieces of 1 KB = LDS columns 2k, 2k+1; wave w issues
@@ -144,13 +158,14 @@ __device__ __forceinline__ void fill_dense(int dst, const unsigned char* kv, int
 }
 
 // sparse: the lane's row id from the LDS ring (-1 = masked -> index out of range)
-__device__ __forceinline__ void fill_sparse(int dst, const i32x4& rs, int row, int fcol, int wave) {
+// sparse: ``src`` is this lane's source (row start + 16 half + 32 wave)
+__device__ __forceinline__ void fill_sparse(int dst, const unsigned char* src, int wave) {
     const int l0 = dst + wave * 1024;
-    dma_struct_x4<0>(rs, row, fcol + 32 * wave, l0);
-    dma_struct_x4<256>(rs, row, fcol + 32 * wave, l0 + 8 * 1024);
-    dma_struct_x4<512>(rs, row, fcol + 32 * wave, l0 + 16 * 1024);
-    dma_struct_x4<768>(rs, row, fcol + 32 * wave, l0 + 24 * 1024);
-    if (wave < 4) dma_struct_x4<0>(rs, row, fcol + 32 * (32 + wave), l0 + 32 * 1024);
+    dma_global_x4<0>(src, l0);
+    dma_global_x4<256>(src, l0 + 8 * 1024);
+    dma_global_x4<512>(src, l0 + 16 * 1024);
+    dma_global_x4<768>(src, l0 + 24 * 1024);
+    if (wave < 4) dma_global_x4<1024>(src, l0 + 32 * 1024);
 }
 
 // ---- FP8 tile fill: the raw 656-B records are copied into the tile buffer
@@ -165,20 +180,6 @@ template <int IMM>
 __device__ __forceinline__ void dma_raw_x1(const i32x4& rs, int voff, int lds) {
     __asm__ volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, 0 offen offset:%3 lds"
                      :: "s"(lds - IMM), "v"(voff), "s"(rs), "i"(IMM) : "memory", "m0");
-}
-// Gathered rows (sparse FP8) are copied with a 64-bit address per lane, so
-// caches beyond 4 GiB are reached (a buffer offset is 32-bit); LDS address =
-// M0 + 16 * lane (x4) or M0 + 4 * lane (x1).  An invalid row reads the zero
-// row below instead, so its bytes land as zeros like an out-of-range buffer
-// load.
-__device__ __align__(16) unsigned char g_zero_row[kFp8RowBytes];   // never written
-__device__ __forceinline__ void dma_global_x4(const unsigned char* src, int lds) {
-    __asm__ volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off"
-                     :: "s"(lds), "v"(src) : "memory", "m0");
-}
-__device__ __forceinline__ void dma_global_x1(const unsigned char* src, int lds) {
-    __asm__ volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, off"
-                     :: "s"(lds), "v"(src) : "memory", "m0");
 }
 __device__ __forceinline__ const unsigned char* fp8_row_addr(const unsigned char* kv, int row, int off) {
     return (row >= 0 ? kv + (int64_t)row * kFp8RowBytes : g_zero_row) + off;
@@ -270,8 +271,9 @@ __device__ __forceinline__ void mstep_schedule_all() {
 // source offset and LDS address of the wave's first piece.
 struct FillCtx {
     bool on;
-    i32x4 rs;
-    int row, vo, l0;
+    i32x4 rs;                    // dense: buffer over the tile's page
+    const unsigned char* src;    // sparse: this lane's source
+    int vo, l0;
 };
 
 template <bool SPARSE, bool FP8>
@@ -321,7 +323,6 @@ __global__ void __launch_bounds__(kThreads, 1) decode_kernel(const DecodeArgs a)
     const int head = hblk * kHeadsPerWG + hb * 32 + l32;   // this lane's head
     const bool head_ok = head < H;
 
-    const i32x4 srs = buffer_rsrc(kv, kRowBytes, (int)a.num_rows);
     const int ftok = l32 ^ (4 * half + 8 * (wave & 1));   // bf16 fill: token this lane copies
     const int fbase = ftok * kRowBytes + 16 * half;       // dense fill source offset (+32k)
     const int fcol = 16 * half;                            // sparse fill column offset (+32k)
@@ -426,7 +427,7 @@ __global__ void __launch_bounds__(kThreads, 1) decode_kernel(const DecodeArgs a)
         auto issue_fill = [&](int it, int page) __attribute__((always_inline)) {
             const int g = g0 + it;
             const int dst = (int)(size_t)(lds_void_t*)&sm.tile[0][0] + opaque_tile_offset(it % kNBuf);
-            if (SPARSE) fill_sparse(dst, srs, sm.rows[it & 3][ftok], fcol, wave);
+            if (SPARSE) fill_sparse(dst, bf16_row_addr(kv, sm.rows[it & 3][ftok], fcol + 32 * wave), wave);
             else {
                 const int ln = lane_id();
                 const int fb = ((ln & 31) ^ (4 * (ln >> 5) + 8 * (wave & 1))) * kRowBytes + 16 * (ln >> 5);
@@ -452,9 +453,9 @@ __global__ void __launch_bounds__(kThreads, 1) decode_kernel(const DecodeArgs a)
                 const int rc = live ? sm.rows[it & 3][tc] : -1;
                 const int rr_ = live ? sm.rows[it & 3][tr] : -1;
                 const int rs_ = (live && l < kSubTok) ? sm.rows[it & 3][l] : -1;
-                dma_global_x4(fp8_row_addr(kv, rc, code_off), code_lds);
-                dma_global_x4(fp8_row_addr(kv, rc, code_off + 32), code_lds + 2048);
-                dma_global_x4(fp8_row_addr(kv, rr_, rope_off), rope_lds);
+                dma_global_x4<0>(fp8_row_addr(kv, rc, code_off), code_lds);
+                dma_global_x4<0>(fp8_row_addr(kv, rc, code_off + 32), code_lds + 2048);
+                dma_global_x4<0>(fp8_row_addr(kv, rr_, rope_off), rope_lds);
                 dma_global_x1(fp8_row_addr(kv, rs_, scale_off), sdst);
             } else {
                 const bool ok = it < ns && page_ok(page, a.num_rows);
@@ -566,15 +567,13 @@ __global__ void __launch_bounds__(kThreads, 1) decode_kernel(const DecodeArgs a)
         // basic block (a branch around each piece makes the compiler wait for
         // every outstanding copy before the next one).
         auto fill_prepare = [&](int t) __attribute__((always_inline)) -> FillCtx {
-            FillCtx f{true, {0, 0, 0, 0}, -1, 0, 0};
+            FillCtx f{true, {0, 0, 0, 0}, nullptr, 0, 0};
             const int g = g0 + t + 1;
             const int w = wave - 4;
             const bool live = t + 1 < ns;
             f.l0 = (int)(size_t)(lds_void_t*)&sm.tile[0][0] + opaque_tile_offset((t + 1) % kNBuf) + 1024 * w;
             if (SPARSE) {
-                f.rs = srs;
-                f.row = live ? sm.rows[(t + 1) & 3][ftok] : -1;
-                f.vo = fcol + 32 * w;
+                f.src = bf16_row_addr(kv, live ? sm.rows[(t + 1) & 3][ftok] : -1, fcol + 32 * w);
             } else if (!live) {
                 f.rs = buffer_rsrc(kv, 0, 0);
                 f.vo = fbase + 32 * w;
@@ -591,11 +590,11 @@ __global__ void __launch_bounds__(kThreads, 1) decode_kernel(const DecodeArgs a)
         auto fill_piece = [&](const FillCtx& f, auto i_c) __attribute__((always_inline)) {
             constexpr int i = decltype(i_c)::value;
             if (f.on) {
-                if (SPARSE) dma_struct_x4<128 * i>(f.rs, f.row, f.vo, f.l0 + 4096 * i);
+                if (SPARSE) dma_global_x4<128 * i>(f.src, f.l0 + 4096 * i);
                 else dma_raw_x4<128 * i>(f.rs, f.vo, f.l0 + 4096 * i);
             }
         };
-        const FillCtx nofill{false, {0, 0, 0, 0}, 0, 0, 0};
+        const FillCtx nofill{false, {0, 0, 0, 0}, nullptr, 0, 0};
         // full scores, mask, exact online softmax.  Register r holds token
         // 8(r/4) + 4*half + r%4 of the tile.  Scores stay unscaled; c > 0 is
         // folded into the exponent.

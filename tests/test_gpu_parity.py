@@ -196,6 +196,20 @@ def test_sparse_small_edge_cases():
     _say(compare(go, gl, ro, rl))
 
 
+def test_sparse_bf16_cache_past_4gib():
+    """A 4.8 GB bf16 cache (2 requests x 2^21 tokens): gathered rows past the
+    first 4 GiB are read through 64-bit addresses, not 32-bit buffer offsets."""
+    from helpers import kv_host_rows
+    _say("sparse bf16 > 4 GiB")
+    w = make_sparse(2, 1, 128, pool_tokens_per_seq=1 << 21, topk=2048, invalid_frac=0.05, seed=71, device=DEV)
+    idx = w.indices.cpu().numpy()
+    assert int((idx.astype(np.int64) * 1152 >= (1 << 32)).sum()) > 100
+    items = [(0, 0), (1, 0)]
+    go, gl, _ = run_library(w)
+    ro, rl = oracle(w, items=items, kv=kv_host_rows(w, items))
+    _say(compare(go, gl, ro, rl, items=items))
+
+
 def test_fp8_small():
     _say("fp8 small")
     w = make_fp8_dense(3, 1, 128, [70, 300, 1], seed=7, device=DEV)
