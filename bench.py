@@ -14,6 +14,11 @@ prefill (mla_sparse_prefill_fwd) of 4096 query rows at the end of a
 32768-row bf16 cache, top-k 2048, 128 heads.  Those lines' roofline is the
 MFMA one.
 
+The same step recorded once into a HIP graph is timed as well
+(``graph_us_per_step``, after a bit-for-bit check of its first replay against
+the eager step); on this path the eager launches are as fast or faster, so
+``value`` is the eager step.
+
 Prints one JSON line.  ``value`` is TFLOP/s of algorithmic work (FLOPs =
 2 h_q (576 + 512) per visible query-token/KV-token pair) per step; the line
 also carries HBM GB/s and microseconds per step, the roofline of the decode
@@ -225,17 +230,22 @@ def main():
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-
     # timed region: exactly K whole steps
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
+    ms_step = _timed(step, args.steps, stream)
+
+    # The step recorded once into a HIP graph (scheduler, decode kernel,
+    # combine) and replayed with one host launch per step; the first replay
+    # must reproduce the eager step bit for bit.
+    ref_out, ref_lse = dec.out.clone(), dec.lse.clone()
+    graph = dec.capture(w.q, w.kv, w.block_table, seqlens, w.indices)
+    dec.out.fill_(3.0)
+    graph.replay()
     torch.cuda.synchronize()
-    e0.record(stream)
-    for _ in range(args.steps):
-        step()
-    e1.record(stream)
-    torch.cuda.synchronize()
-    ms_step = e0.elapsed_time(e1) / args.steps
+    assert torch.equal(dec.out.view(torch.int16), ref_out.view(torch.int16)) and torch.equal(dec.lse, ref_lse), \
+        "graph replay differs from the eager step"
+    for _ in range(args.warmup):
+        graph.replay()
+    ms_graph = _timed(graph.replay, args.steps, stream)
 
     # decode call alone (partial-attention kernel + combine), same stream, same inputs
     k0 = torch.cuda.Event(enable_timing=True)
@@ -284,6 +294,7 @@ def main():
         "warmup": args.warmup,
         "ms_per_step": round(ms_step, 5),
         "us_per_step": round(ms_step * 1e3, 2),
+        "graph_us_per_step": round(ms_graph * 1e3, 2),
         "hbm_gbs": round(gbs, 1),
         "higher_is_better": True,
         "scaling": "weak",
@@ -293,7 +304,8 @@ def main():
         "config": {"workload": "dense absorbed-MLA decode b=64 s_q=1 h_q=128 seqlen=4096 (64-token pages, "
                                "4096-page shuffled pool, bf16 q/kv N(0,1))",
                    "batch": w.batch, "s_q": w.s_q, "h_q": w.h_q, "seqlen": 4096, "d_qk": 576, "d_v": 512,
-                   "block_size": 64, "kv_format": "bf16", "step": "metadata + decode (partial + combine)"},
+                   "block_size": 64, "kv_format": "bf16",
+                   "step": "metadata + decode (partial + combine)"},
         "roofline": {"bound": "hbm", "kernel": "decode_kernel<dense, bf16 cache> (partial attention)",
                      "achieved": round(kern_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(kern_gbs / HBM_PEAK_GBS, 4), "traffic": measured_traffic(),
@@ -310,7 +322,8 @@ def main():
                                       f"(656-byte records, {max(32768, 2 * topk)} cached tokens per request, "
                                       "every slot valid, N(0,1) sources)",
                           "batch": w.batch, "s_q": w.s_q, "h_q": w.h_q, "topk": topk, "d_qk": 576, "d_v": 512,
-                          "block_size": 64, "kv_format": "fp8_656", "step": "metadata + sparse decode (partial + combine)"}
+                          "block_size": 64, "kv_format": "fp8_656",
+                          "step": "metadata + sparse decode (partial + combine)"}
         line["roofline"] = {"bound": "mfma", "kernel": "decode_kernel<sparse, fp8 cache> (partial attention)",
                             "achieved": round(kern_tflops, 1), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                             "frac": round(kern_tflops / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,

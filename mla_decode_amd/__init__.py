@@ -265,6 +265,22 @@ class Decoder:
         self.metadata(cache_seqlens, stream, topk_length)
         return self.decode(q, kv_cache, block_table, cache_seqlens, indices, stream, topk_length, attn_sink)
 
+    def capture(self, q, kv_cache, block_table=None, cache_seqlens=None, indices=None, topk_length=None,
+                attn_sink=None):
+        """Record one whole step (scheduler, decode kernel, combine) into a HIP graph and return it;
+        ``graph.replay()`` reruns the step on the same tensors with a single launch from the host.
+        The step records no memset node; the tensors must stay allocated while the graph is used."""
+        side = torch.cuda.Stream(device=self.out.device)
+        side.wait_stream(torch.cuda.current_stream(self.out.device))
+        with torch.cuda.stream(side):          # warm the launch path outside the capture
+            self.step(q, kv_cache, block_table, cache_seqlens, indices, side, topk_length, attn_sink)
+        torch.cuda.current_stream(self.out.device).wait_stream(side)
+        torch.cuda.synchronize(self.out.device)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            self.step(q, kv_cache, block_table, cache_seqlens, indices, None, topk_length, attn_sink)
+        return g
+
     @classmethod
     def for_workload(cls, w, device="cuda", num_cus=0, rescale_threshold=0.0):
         p = make_problem(w.batch, w.s_q, w.h_q, w.num_blocks, w.max_blocks_per_seq, topk=w.topk, causal=w.causal,
