@@ -54,3 +54,38 @@ def dequant_records(rec):
     rope = bf16_bits_to_f64(rope_bits)
     out = np.concatenate([latent, rope], axis=1)
     return out.reshape(lead + (LATENT + ROPE,))
+
+
+# --------------------------------------------------------------------------
+# The 528-byte record of the newer model (FlashMLA README copy, "FP8 / FP4 KV
+# Cache Format"): head_dim 512 with the 64 RoPE dimensions quantised as well;
+# per token 512 float8_e4m3 values, then 16 float8_e8m0 scales, one for every
+# 32 consecutive values; no bfloat16 part.  K and V are both the 512 values.
+#
+# Readings: an e8m0 byte e is the power of two 2^(e - 127), with e = 255 NaN
+# (the OCP "E8M0" scale format); the dequantised value e4m3(x) * 2^(e - 127)
+# is exact in float64, and also in bfloat16 unless it leaves bfloat16's
+# exponent range, so it is returned unrounded.
+
+V41_RECORD_BYTES = 528
+V41_DIM = 512
+V41_GROUP = 32
+
+
+def e8m0_decode(e):
+    """float8_e8m0 bytes -> float64: 2^(e - 127), NaN for 255."""
+    e = np.asarray(e, dtype=np.int64)
+    out = np.ldexp(1.0, e - 127)
+    return np.where(e == 255, np.nan, out)
+
+
+def dequant_records_v41(rec):
+    """uint8 records [..., 528] -> float64 K (= V) values [..., 512]."""
+    rec = np.asarray(rec, dtype=np.uint8)
+    assert rec.shape[-1] == V41_RECORD_BYTES
+    lead = rec.shape[:-1]
+    flat = np.ascontiguousarray(rec.reshape(-1, V41_RECORD_BYTES))
+    vals = e4m3fn_decode(flat[:, :V41_DIM]).astype(np.float64)
+    scales = e8m0_decode(flat[:, V41_DIM:])                      # [n, 16]
+    out = vals * np.repeat(scales, V41_GROUP, axis=1)
+    return out.reshape(lead + (V41_DIM,))

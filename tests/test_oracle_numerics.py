@@ -63,3 +63,58 @@ def test_dequant_against_torch_conversions():
     err = np.abs(got[:, :512] - x[:, :512].numpy())
     amax = np.abs(x[:, :512].numpy()).reshape(300, 4, 128).max(axis=2)
     assert np.all(err.reshape(300, 4, 128) <= (amax / 448.0 * 16.0 + amax * 2.0 ** -8 + 1e-6)[:, :, None])
+
+
+# ------------------------------------------------------------------ the 528-byte record (512-wide head)
+
+def test_e8m0_all_codes_closed_form_and_library():
+    e = np.arange(256, dtype=np.uint8)
+    got = F8.e8m0_decode(e)
+    lib = torch.from_numpy(e.copy()).view(torch.float8_e8m0fnu).to(torch.float64).numpy()
+    for c in range(255):
+        assert got[c] == 2.0 ** (c - 127) == lib[c]
+    assert np.isnan(got[255]) and np.isnan(lib[255])
+
+
+def test_v41_record_layout_matches_pages():
+    # 512 e4m3 values, then one e8m0 scale for every 32 values: 512 + 16 bytes
+    assert F8.V41_RECORD_BYTES == 512 * 1 + (512 // 32) * 1 == 528
+
+
+def test_v41_dequant_against_torch_conversions():
+    from workloads.gen import encode_v41_records
+    g = torch.Generator().manual_seed(5)
+    x = torch.randn(300, 512, generator=g) * torch.logspace(-3, 3, 512)[None, :]   # spread of group scales
+    x[7, 64:96] = 0.0                                                                # an all-zero group
+    rec = encode_v41_records(x).numpy()
+    got = F8.dequant_records_v41(rec)
+    codes = torch.from_numpy(rec[:, :512].copy()).view(torch.float8_e4m3fn).to(torch.float64)
+    scales = torch.from_numpy(rec[:, 512:].copy()).view(torch.float8_e8m0fnu).to(torch.float64)
+    ref = (codes.view(300, 16, 32) * scales[..., None]).view(300, 512).numpy()
+    assert np.array_equal(got, ref)
+    # the encoder's power-of-two scales keep every code finite and within e4m3's precision of x
+    xs = x.double().numpy()
+    assert np.all(np.isfinite(got))
+    assert np.all(np.abs(got - xs) <= 2.0 ** -4 * np.abs(xs) + np.repeat(F8.e8m0_decode(rec[:, 512:]), 32, 1) * 2.0 ** -9)
+    assert np.all(got[7, 64:96] == 0.0)
+
+
+def test_v41_decode_is_attention_over_the_dequantised_rows():
+    """The oracle's decode over 528-byte records equals the plain two-pass
+    attention over the dequantised 512-wide rows, with V = K."""
+    from oracle import attention as A
+    from workloads import make_v41_sparse
+    w = make_v41_sparse(2, 1, 4, pool_tokens_per_seq=256, topk=40, invalid_frac=0.1, seed=9)
+    q = w.q.contiguous().view(torch.int16).numpy().view(np.uint16)
+    kv = w.kv.numpy().reshape(-1, 528)
+    idx = w.indices.numpy()
+    out, lse = A.decode(q, kv, w.softmax_scale, indices=idx, kv_format='fp8_528')
+    for b in range(2):
+        rows = idx[b, 0][idx[b, 0] >= 0]
+        K = F8.dequant_records_v41(kv[rows])
+        qh = Nm.bf16_bits_to_f64(q[b, 0])
+        s = w.softmax_scale * qh @ K.T
+        m = s.max(axis=1, keepdims=True)
+        p = np.exp(s - m)
+        assert np.max(np.abs(out[b, 0] - (p @ K) / p.sum(axis=1, keepdims=True))) < 1e-12
+        assert np.max(np.abs(lse[b, :, 0] - (m[:, 0] + np.log(p.sum(axis=1))))) < 1e-12

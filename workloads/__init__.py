@@ -4,5 +4,6 @@ only random numbers, paged block tables, top-k index lists and the FP8 cache
 encoder that turns random values into 656-byte records."""
 
 from .gen import (Workload, make_config, make_dense, make_sparse, make_fp8_dense,  # noqa: F401
-                  make_fp8_sparse, make_sparse_prefill, PrefillWorkload, CONFIG_NAMES)
+                  make_fp8_sparse, make_sparse_prefill, PrefillWorkload, make_v41_sparse, encode_v41_records,
+                  CONFIG_NAMES)
 from .accounting import flops_and_bytes  # noqa: F401

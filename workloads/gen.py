@@ -218,6 +218,47 @@ def make_sparse(batch, s_q, h_q, *, pool_tokens_per_seq, topk, invalid_frac=0.05
                     indices=indices, meta={'peaked': peaked, 'order': order})
 
 
+V41_RECORD = 528
+
+
+def encode_v41_records(x):
+    """float32 [n, 512] -> uint8 [n, 528]: per group of 32 values the smallest power of two 2^(e-127) with
+    amax / 2^(e-127) <= 448 (e = 127 for an all-zero group), the codes float8_e4m3fn(x / 2^(e-127)) (torch's
+    round-to-nearest cast after clamping to +-448), then the 16 exponent bytes e."""
+    n = x.shape[0]
+    g = x.view(n, 16, 32)
+    amax = g.abs().amax(dim=-1)
+    e = torch.where(amax > 0, torch.ceil(torch.log2(amax / 448.0)), torch.zeros_like(amax)) + 127
+    e = e.clamp(0, 254)
+    scale = torch.pow(2.0, e - 127)
+    # the log2 above can land one short: move up until every value fits
+    e = torch.where(amax / scale > 448.0, e + 1, e)
+    scale = torch.pow(2.0, e - 127)
+    codes = (g / scale[..., None]).clamp(-448.0, 448.0).to(torch.float8_e4m3fn).view(torch.uint8).reshape(n, 512)
+    return torch.cat([codes, e.to(torch.uint8)], dim=1)
+
+
+def make_v41_sparse(batch, s_q, h_q, *, pool_tokens_per_seq, topk, invalid_frac=0.0, seed=0, device='cpu',
+                    name='v41_sparse'):
+    """Top-k decode inputs over the 528-byte records of the 512-wide head (RoPE dims quantised too): q is
+    [batch, s_q, h_q, 512]; cache values N(0, 1) encoded by ``encode_v41_records``; indices as for
+    ``make_sparse``."""
+    w = make_sparse(batch, s_q, h_q, pool_tokens_per_seq=pool_tokens_per_seq, topk=topk, invalid_frac=invalid_frac,
+                    seed=seed, device=device, name=name)
+    nb = w.num_blocks
+    g = _gen(device, seed + 104729)
+    kv = torch.empty((nb, BLOCK, 1, V41_RECORD), dtype=torch.uint8, device=device)
+    for s in range(0, nb, 256):
+        e = min(nb, s + 256)
+        x = torch.randn(((e - s) * BLOCK, 512), generator=g, device=device)
+        kv[s:e] = encode_v41_records(x).view(e - s, BLOCK, 1, V41_RECORD)
+    w.kv = kv
+    w.kv_format = 'fp8_528'
+    w.q = _randn_bf16((batch, s_q, h_q, 512), g, device, chunk_rows=64)
+    w.softmax_scale = 1.0 / math.sqrt(512)
+    return w
+
+
 def make_fp8_sparse(topk, device='cpu', seed=None, batch=128, s_q=2, h_q=128):
     """The FP8 sparse decode shape the pages quote for the H800 kernel: 128
     requests, 2 query tokens each, 128 heads, top-k 2048 or 32768 over a
