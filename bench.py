@@ -80,11 +80,11 @@ def cpu_baseline_sparse(w):
         for i in range(w.s_q):
             rows = idx[b, i][(idx[b, i] >= 0) & (idx[b, i] < nrows)]
             got = kv_rows[torch.from_numpy(rows.astype(np.int64)).to(w.kv.device)].cpu()   # gathered on the GPU
-            kv = got.numpy() if w.kv_format == "fp8" else got.view(torch.int16).numpy().view(np.uint16)
+            kv = got.numpy() if w.kv_format.startswith("fp8") else got.view(torch.int16).numpy().view(np.uint16)
             t0 = time.perf_counter()
             A.decode_partial(q, kv, w.softmax_scale, np.arange(len(rows)), b, i, kv_format=w.kv_format)
             dt += time.perf_counter() - t0
-            flops += 2.0 * w.h_q * (576 + 512) * len(rows)
+            flops += 2.0 * w.h_q * (int(w.q.shape[-1]) + 512) * len(rows)
             done += 1
             if dt >= 10.0:
                 break
@@ -184,7 +184,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--workload", default="dense_b64_s4096",
-                    choices=["dense_b64_s4096", "fp8_sparse_topk2048", "fp8_sparse_topk32768", "sparse_prefill"],
+                    choices=["dense_b64_s4096", "fp8_sparse_topk2048", "fp8_sparse_topk32768", "sparse_prefill",
+                             "v41_sparse_topk2048"],
                     help="dense_b64_s4096 is the headline line; the others time the pages' FP8 sparse shape")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a 1 GiB device copy 5 times (reference for HBM byte counters)")
@@ -206,7 +207,7 @@ def main():
 
     import torch
     import mla_decode_amd as mla
-    from workloads import make_config, make_fp8_sparse, flops_and_bytes
+    from workloads import make_config, make_fp8_sparse, make_v41_sparse, flops_and_bytes
 
     if args.workload == "sparse_prefill":
         return bench_prefill(args)
@@ -216,6 +217,9 @@ def main():
     headline = args.workload == "dense_b64_s4096"
     if headline:
         w = make_config(2, device=dev)
+    elif args.workload.startswith("v41"):
+        w = make_v41_sparse(128, 2, 128, pool_tokens_per_seq=32768, topk=2048, seed=4000, device=dev,
+                            name="v41_sparse_b128_s2_topk2048")
     else:
         w = make_fp8_sparse(int(args.workload.split("topk")[1]), device=dev)
     acct = flops_and_bytes(w)
@@ -317,12 +321,16 @@ def main():
     }
     if not headline:
         topk = w.topk
-        line["metric"] = f"MLA sparse FP8 decode TFLOPS, µs/step at b=128,s_q=2,h_q=128,topk={topk} (1 GPU)"
+        v41 = w.kv_format == "fp8_528"
+        rec = "528-byte records of the 512-wide head (e8m0 scales per 32 values)" if v41 else "656-byte records"
+        line["metric"] = (f"MLA sparse FP8 decode TFLOPS, µs/step at b=128,s_q=2,h_q=128,topk={topk}"
+                          f"{',528B records,d_qk=512' if v41 else ''} (1 GPU)")
         line["config"] = {"workload": f"FP8 sparse absorbed-MLA decode b=128 s_q=2 h_q=128 top-k {topk} "
-                                      f"(656-byte records, {max(32768, 2 * topk)} cached tokens per request, "
+                                      f"({rec}, {max(32768, 2 * topk)} cached tokens per request, "
                                       "every slot valid, N(0,1) sources)",
-                          "batch": w.batch, "s_q": w.s_q, "h_q": w.h_q, "topk": topk, "d_qk": 576, "d_v": 512,
-                          "block_size": 64, "kv_format": "fp8_656",
+                          "batch": w.batch, "s_q": w.s_q, "h_q": w.h_q, "topk": topk,
+                          "d_qk": 512 if v41 else 576, "d_v": 512,
+                          "block_size": 64, "kv_format": "fp8_528" if v41 else "fp8_656",
                           "step": "metadata + sparse decode (partial + combine)"}
         line["roofline"] = {"bound": "mfma", "kernel": "decode_kernel<sparse, fp8 cache> (partial attention)",
                             "achieved": round(kern_tflops, 1), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",

@@ -61,12 +61,17 @@ typedef enum {
 
 typedef enum {
     MLA_KV_BF16_576 = 0,  /* 576 bfloat16 per token (1152 B)                        */
-    MLA_KV_FP8_656 = 1    /* 512 e4m3fn | 4 float32 scales (1 per 128) | 64 bf16   */
+    MLA_KV_FP8_656 = 1,   /* 512 e4m3fn | 4 float32 scales (1 per 128) | 64 bf16   */
+    /* 512 e4m3fn | 16 float8_e8m0 scales (1 per 32 values): the 512-wide head of
+     * the README copy's newer model, RoPE dims quantised too (README copy, "FP8 /
+     * FP4 KV Cache Format").  d_qk = d_v = 512 (K and V are the same 512
+     * values), q is [batch, s_q, h_q, 512]; top-k sparse problems only. */
+    MLA_KV_FP8_528 = 2
 } mla_kv_format_t;
 
 typedef enum { MLA_OUT_BF16 = 0, MLA_OUT_FP32 = 1 } mla_out_dtype_t;
 
-/* Problem shape.  Supported: h_kv = 1, d_qk = 576, d_v = 512, block_size = 64
+/* Problem shape.  Supported: h_kv = 1, d_qk = 576 (512 for MLA_KV_FP8_528), d_v = 512, block_size = 64
  * (FlashMLA README: the key cache has one head; d_v can only be 512).  Tensor
  * layouts:
  *   q            [batch, s_q, h_q, 576]              bfloat16

@@ -16,6 +16,7 @@ STATUS_NAMES = {0: "MLA_OK", 1: "MLA_ERR_INVALID_ARG", 2: "MLA_ERR_UNSUPPORTED",
                 4: "MLA_ERR_METADATA_MISMATCH", 5: "MLA_ERR_HIP"}
 KV_BF16_576 = 0
 KV_FP8_656 = 1
+KV_FP8_528 = 2
 OUT_BF16 = 0
 OUT_FP32 = 1
 

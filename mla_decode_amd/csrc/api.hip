@@ -41,12 +41,16 @@ mla_status_t validate(const mla_problem_t* p) {
     if (p->batch < 1 || p->s_q < 1 || p->h_q < 1 || p->num_blocks < 1) return MLA_ERR_INVALID_ARG;
     if (p->topk < 0 || p->max_blocks_per_seq < 0) return MLA_ERR_INVALID_ARG;
     if (p->causal != 0 && p->causal != 1) return MLA_ERR_INVALID_ARG;
-    if (p->kv_format != MLA_KV_BF16_576 && p->kv_format != MLA_KV_FP8_656) return MLA_ERR_INVALID_ARG;
+    if (p->kv_format != MLA_KV_BF16_576 && p->kv_format != MLA_KV_FP8_656 && p->kv_format != MLA_KV_FP8_528)
+        return MLA_ERR_INVALID_ARG;
     if (p->out_dtype != MLA_OUT_BF16 && p->out_dtype != MLA_OUT_FP32) return MLA_ERR_INVALID_ARG;
     if (!std::isfinite(p->softmax_scale) || !(p->softmax_scale > 0.f)) return MLA_ERR_INVALID_ARG;
     if (!(p->rescale_threshold >= 0.f && p->rescale_threshold <= 30.f)) return MLA_ERR_INVALID_ARG;
-    if (p->h_kv != 1 || p->d_qk != mla::kDqk || p->d_v != mla::kDv || p->block_size != kBlock)
+    // the 528-byte records carry the 512-wide head (K = V), read through top-k indices
+    const int d_qk = p->kv_format == MLA_KV_FP8_528 ? 512 : mla::kDqk;
+    if (p->h_kv != 1 || p->d_qk != d_qk || p->d_v != mla::kDv || p->block_size != kBlock)
         return MLA_ERR_UNSUPPORTED;
+    if (p->kv_format == MLA_KV_FP8_528 && p->topk < 1) return MLA_ERR_UNSUPPORTED;
     if (p->topk == 0 && p->max_blocks_per_seq < 1) return MLA_ERR_INVALID_ARG;
     if (p->topk > 0 && p->causal) return MLA_ERR_UNSUPPORTED;
     const int64_t items = (int64_t)p->batch * p->s_q;
@@ -138,7 +142,7 @@ mla_status_t run_decode(const mla_problem_t* p, bool sparse, const void* q, cons
     a.scale_log2 = p->softmax_scale * 1.4426950408889634f;
     a.rescale_tau = p->rescale_threshold;
     hipStream_t s = (hipStream_t)stream;
-    if (mla::launch_decode(a, sparse, p->kv_format == MLA_KV_FP8_656, s) != hipSuccess) return MLA_ERR_HIP;
+    if (mla::launch_decode(a, sparse, p->kv_format, s) != hipSuccess) return MLA_ERR_HIP;
 
     mla::CombineArgs c{};
     c.o_part = a.o_part;

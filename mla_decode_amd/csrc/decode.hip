@@ -181,8 +181,15 @@ __device__ __forceinline__ void dma_raw_x1(const i32x4& rs, int voff, int lds) {
     __asm__ volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, 0 offen offset:%3 lds"
                      :: "s"(lds - IMM), "v"(voff), "s"(rs), "i"(IMM) : "memory", "m0");
 }
-__device__ __forceinline__ const unsigned char* fp8_row_addr(const unsigned char* kv, int row, int off) {
-    return (row >= 0 ? kv + (int64_t)row * kFp8RowBytes : g_zero_row) + off;
+// ``rec``: record bytes (656, or 528 for the 512-wide head)
+__device__ __forceinline__ const unsigned char* fp8_row_addr(const unsigned char* kv, int row, int off, int rec) {
+    return (row >= 0 ? kv + (int64_t)row * rec : g_zero_row) + off;
+}
+
+// float8_e8m0 scale byte -> 2^(e - 127) (e = 255: NaN)
+__device__ __forceinline__ float e8m0_scale(unsigned e) {
+    if (e == 255u) return __uint_as_float(0x7FC00000u);
+    return e == 0u ? __uint_as_float(0x00400000u) : __uint_as_float(e << 23);
 }
 
 // LDS token slot of lane l in a copy of columns (c, c+1): column c + (l >> 5),
@@ -191,12 +198,15 @@ __device__ __forceinline__ int fp8_code_token(int l) { return (l & 31) ^ (8 + 4 
 __device__ __forceinline__ int fp8_rope_token(int l, int w) { return (l & 31) ^ (4 * (l >> 5) + 8 * (w & 1)); }
 
 // e4m3fn -> fp32 (exact), x scale in fp32, -> bf16 (round to nearest even), in
-// place: lane l of wave w converts part 2w + (l >> 5) of token l & 31.
+// place: lane l of wave w converts part 2w + (l >> 5) of token l & 31.  The
+// scale word of a token holds one float32 (656-byte record: dims 128s..) or,
+// for the 528-byte record, four e8m0 bytes of parts 4s..4s+3 (32 dims each).
+template <bool E8M0>
 __device__ __forceinline__ void fp8_convert(unsigned char* dst, const float* scales, int w, int l) {
     const int t = l & 31, p = 2 * w + (l >> 5);
     const i32x4 raw[2] = {*(const i32x4*)(dst + lds_chunk(t, 4 * p + 2) * 16),
                           *(const i32x4*)(dst + lds_chunk(t, 4 * p + 3) * 16)};
-    const float sc = scales[t];
+    const float sc = E8M0 ? e8m0_scale((__float_as_uint(scales[t]) >> (8 * (p & 3))) & 0xFFu) : scales[t];
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
         float v[16];
@@ -259,12 +269,12 @@ constexpr int mstep_first_reads() {
     else return 0;
 }
 
-template <int I0, int I1>
+template <int I0, int I1, bool QK>
 __device__ __forceinline__ void mstep_schedule_all() {
     constexpr int first = mstep_first_reads<I0, (I1 < I0 + kMstepLookahead ? I1 : I0 + kMstepLookahead)>();
     __builtin_amdgcn_sched_group_barrier(kSchedDsRead, first, 0);
     mstep_schedule<I0, I1>();
-    if constexpr (I1 == 34) __builtin_amdgcn_sched_group_barrier(kSchedDsWrite, 4, 0);
+    if constexpr (QK) __builtin_amdgcn_sched_group_barrier(kSchedDsWrite, 4, 0);
 }
 
 // A tile copy to be issued piecewise: buffer resource, sparse row id, lane
@@ -276,8 +286,15 @@ struct FillCtx {
     int vo, l0;
 };
 
-template <bool SPARSE, bool FP8>
+// KVF: cache format, 0 = bf16 rows of 576, 1 = 656-byte FP8 records, 2 =
+// 528-byte FP8 records of the 512-wide head (K = V = all 512 dims, no RoPE part)
+template <bool SPARSE, int KVF>
 __global__ void __launch_bounds__(kThreads, 1) decode_kernel(const DecodeArgs a) {
+    constexpr bool FP8 = KVF != 0;
+    constexpr bool D512 = KVF == 2;
+    constexpr int kQRow = D512 ? 1024 : kRowBytes;            // q row bytes
+    constexpr int kRec = D512 ? 528 : kFp8RowBytes;           // FP8 record bytes
+    static_assert(!D512 || SPARSE, "the 528-byte records are read through top-k indices");
     __shared__ Smem sm;
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -387,7 +404,7 @@ __global__ void __launch_bounds__(kThreads, 1) decode_kernel(const DecodeArgs a)
             const int head_o = hblk * kHeadsPerWG + hb * 32 + (tid_o & 31);
             const int half_o = (tid_o >> 5) & 1;
             const bf16x8* qp = (const bf16x8*)((const unsigned char*)a.q +
-                                               ((int64_t)j * H + (head_o < H ? head_o : 0)) * kRowBytes);
+                                               ((int64_t)j * H + (head_o < H ? head_o : 0)) * kQRow);
 #pragma unroll
             for (int kk = 0; kk < 16; ++kk) {
                 bf16x8 v = qp[32 * kh + 2 * kk + half_o];
@@ -400,8 +417,8 @@ __global__ void __launch_bounds__(kThreads, 1) decode_kernel(const DecodeArgs a)
                 const int ln = idx & 63, kr = (idx >> 6) & 3, hb2 = idx >> 8;
                 const int hq = hblk * kHeadsPerWG + hb2 * 32 + (ln & 31);
                 bf16x8 v = {};
-                if (hq < H)
-                    v = ((const bf16x8*)((const unsigned char*)a.q + ((int64_t)j * H + hq) * kRowBytes))[64 + 2 * kr + (ln >> 5)];
+                if (!D512 && hq < H)
+                    v = ((const bf16x8*)((const unsigned char*)a.q + ((int64_t)j * H + hq) * kQRow))[64 + 2 * kr + (ln >> 5)];
                 qrv[e] = v;
             }
         }
@@ -453,10 +470,10 @@ __global__ void __launch_bounds__(kThreads, 1) decode_kernel(const DecodeArgs a)
                 const int rc = live ? sm.rows[it & 3][tc] : -1;
                 const int rr_ = live ? sm.rows[it & 3][tr] : -1;
                 const int rs_ = (live && l < kSubTok) ? sm.rows[it & 3][l] : -1;
-                dma_global_x4<0>(fp8_row_addr(kv, rc, code_off), code_lds);
-                dma_global_x4<0>(fp8_row_addr(kv, rc, code_off + 32), code_lds + 2048);
-                dma_global_x4<0>(fp8_row_addr(kv, rr_, rope_off), rope_lds);
-                dma_global_x1(fp8_row_addr(kv, rs_, scale_off), sdst);
+                dma_global_x4<0>(fp8_row_addr(kv, rc, code_off, kRec), code_lds);
+                dma_global_x4<0>(fp8_row_addr(kv, rc, code_off + 32, kRec), code_lds + 2048);
+                if (!D512) dma_global_x4<0>(fp8_row_addr(kv, rr_, rope_off, kRec), rope_lds);
+                dma_global_x1(fp8_row_addr(kv, rs_, scale_off, kRec), sdst);
             } else {
                 const bool ok = it < ns && page_ok(page, a.num_rows);
                 int nvalid = min(nslots - g * kSubTok, kSubTok);
@@ -470,7 +487,7 @@ __global__ void __launch_bounds__(kThreads, 1) decode_kernel(const DecodeArgs a)
             }
         };
         auto fp8_dequant = [&](int it) __attribute__((always_inline)) {
-            fp8_convert(sm.tile[0] + opaque_tile_offset(it % kNBuf), sm.f8scale[wave], wave, lane_id());
+            fp8_convert<D512>(sm.tile[0] + opaque_tile_offset(it % kNBuf), sm.f8scale[wave], wave, lane_id());
         };
         // tile 0 lands before step 0
         if (FP8) {
@@ -483,7 +500,7 @@ __global__ void __launch_bounds__(kThreads, 1) decode_kernel(const DecodeArgs a)
 #pragma unroll
         for (int e = 0; e < 2; ++e) {
             const int idx = tid + kThreads * e;
-            sm.qr[idx >> 8][(idx >> 6) & 3][idx & 63] = qrv[e];
+            if (!D512) sm.qr[idx >> 8][(idx >> 6) & 3][idx & 63] = qrv[e];
         }
         if (!FP8) __builtin_amdgcn_s_waitcnt(0x0F70);
         lds_barrier();
@@ -512,7 +529,7 @@ __global__ void __launch_bounds__(kThreads, 1) decode_kernel(const DecodeArgs a)
             constexpr bool DO_PV = decltype(pv_c)::value != 0;
             constexpr bool DO_QK = decltype(qk_c)::value != 0;
             constexpr int I0 = DO_PV ? 0 : 16;
-            constexpr int I1 = DO_QK ? 34 : 16;
+            constexpr int I1 = DO_QK ? (D512 ? 32 : 34) : 16;   // the 512-wide head has no RoPE steps
             const unsigned char* Tp = sm.tile[0] + opaque_tile_offset((t + kNBuf - 1) % kNBuf) + 16384 * kh;  // t-1
             const unsigned char* T = sm.tile[0] + opaque_tile_offset(t % kNBuf);                               // t
             auto fetch = [&](int i, bf16x8& A, bf16x8& B) __attribute__((always_inline)) {
@@ -556,7 +573,7 @@ __global__ void __launch_bounds__(kThreads, 1) decode_kernel(const DecodeArgs a)
                 for (int i = 0; i < 4; ++i)
                     sm.xs[hb][kh][i][lane] = f32x4{s[4 * i], s[4 * i + 1], s[4 * i + 2], s[4 * i + 3]};
             }
-            mstep_schedule_all<I0, I1>();
+            mstep_schedule_all<I0, I1, DO_QK>();
         };
         // Copy of tile t+1 into the buffer of tile t-2, issued by group 1 during
         // its softmax step 2t: wave 4 + w issues the nine 1-KiB pieces w + 4i,
@@ -781,14 +798,15 @@ __global__ void __launch_bounds__(kThreads, 1) decode_kernel(const DecodeArgs a)
     }
 }
 
-hipError_t launch_decode(const DecodeArgs& a, bool sparse, bool fp8, hipStream_t stream) {
+hipError_t launch_decode(const DecodeArgs& a, bool sparse, int kvf, hipStream_t stream) {
     const dim3 grid(a.num_parts * a.n_hblk), block(kThreads);
     if (sparse) {
-        if (fp8) hipLaunchKernelGGL((decode_kernel<true, true>), grid, block, 0, stream, a);
-        else hipLaunchKernelGGL((decode_kernel<true, false>), grid, block, 0, stream, a);
+        if (kvf == 2) hipLaunchKernelGGL((decode_kernel<true, 2>), grid, block, 0, stream, a);
+        else if (kvf == 1) hipLaunchKernelGGL((decode_kernel<true, 1>), grid, block, 0, stream, a);
+        else hipLaunchKernelGGL((decode_kernel<true, 0>), grid, block, 0, stream, a);
     } else {
-        if (fp8) hipLaunchKernelGGL((decode_kernel<false, true>), grid, block, 0, stream, a);
-        else hipLaunchKernelGGL((decode_kernel<false, false>), grid, block, 0, stream, a);
+        if (kvf == 1) hipLaunchKernelGGL((decode_kernel<false, 1>), grid, block, 0, stream, a);
+        else hipLaunchKernelGGL((decode_kernel<false, 0>), grid, block, 0, stream, a);
     }
     return hipGetLastError();
 }

@@ -50,7 +50,8 @@ struct GatherArgs {
     int batch, s_q, max_blocks, topk, causal, row_stride;
 };
 
-hipError_t launch_decode(const DecodeArgs& a, bool sparse, bool fp8, hipStream_t stream);
+// kvf: 0 = bf16 rows of 576, 1 = 656-byte FP8 records, 2 = 528-byte FP8 records (512-wide head, sparse only)
+hipError_t launch_decode(const DecodeArgs& a, bool sparse, int kvf, hipStream_t stream);
 hipError_t launch_metadata(const MetaArgs& a, hipStream_t stream);
 hipError_t launch_combine(const CombineArgs& a, hipStream_t stream);
 hipError_t launch_gather(const GatherArgs& a, hipStream_t stream);

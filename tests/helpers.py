@@ -36,10 +36,11 @@ def kv_host_rows(w, items):
     nrows = rows_dev.shape[0]
     idx = w.indices.cpu().numpy()
     need = np.unique(np.concatenate([idx[b, i][(idx[b, i] >= 0) & (idx[b, i] < nrows)] for b, i in items]))
-    host = np.zeros((nrows, rows_dev.shape[1]), dtype=np.uint8 if w.kv_format == 'fp8' else np.uint16)
+    raw = w.kv_format.startswith('fp8')        # byte records; bf16 rows otherwise
+    host = np.zeros((nrows, rows_dev.shape[1]), dtype=np.uint8 if raw else np.uint16)
     sel = torch.from_numpy(need.astype(np.int64)).to(w.kv.device)
     got = rows_dev[sel].cpu()
-    host[need] = got.numpy() if w.kv_format == 'fp8' else got.view(torch.int16).numpy().view(np.uint16)
+    host[need] = got.numpy() if raw else got.view(torch.int16).numpy().view(np.uint16)
     return host
 
 

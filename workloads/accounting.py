@@ -3,10 +3,11 @@
 Counting rules (FlashMLA new-kernel deep dive, "Theoretical analysis"; MLA
 cost-analysis page, "FlashMLA" cost model):
 * FLOPs = 2 * h_q * (d_k + d_v) per (query token, visible KV token) pair,
-  d_k = 576, d_v = 512; top-k decode counts valid slots only;
-* bytes = every KV row a request needs, read once (1152 B bf16, 656 B FP8),
-  plus q (576 bf16 per head), out (512 per head, 2 or 4 B), lse (4 B per
-  head), and the block table or top-k indices (4 B each).
+  d_k = 576 (512 for the 528-byte records), d_v = 512; top-k decode counts
+  valid slots only;
+* bytes = every KV row a request needs, read once (1152 B bf16, 656 B or
+  528 B FP8), plus q (d_k bf16 per head), out (512 per head, 2 or 4 B), lse
+  (4 B per head), and the block table or top-k indices (4 B each).
 Split partials and scheduler metadata are implementation overhead and are not
 counted here.  ``partial_bytes`` (KV rows, q, table or indices) is what the
 partial-attention kernel alone must move; the outputs of split items are
@@ -31,7 +32,8 @@ def visible(L, s_q, i, causal):
 def flops_and_bytes(w):
     """Algorithmic FLOPs and HBM bytes of one decode call on workload ``w``."""
     B, S, H = w.batch, w.s_q, w.h_q
-    row_bytes = 1152 if w.kv_format == 'bf16' else 656
+    row_bytes = {'bf16': 1152, 'fp8': 656, 'fp8_528': 528}[w.kv_format]
+    d_qk = 512 if w.kv_format == 'fp8_528' else D_QK
     out_elem = 2 if w.out_dtype == 'bf16' else 4
     if w.topk:
         idx = w.indices.to('cpu').to(torch.int64)
@@ -47,9 +49,9 @@ def flops_and_bytes(w):
         pairs = sum(visible(L, S, i, w.causal) for L in lens for i in range(S))
         kv_rows = sum(lens)
         side = sum(math.ceil(L / BLOCK) for L in lens) * 4
-    flops = 2.0 * H * (D_QK + D_V) * pairs
+    flops = 2.0 * H * (d_qk + D_V) * pairs
     kv_bytes = kv_rows * row_bytes
-    q_bytes = B * S * H * D_QK * 2
+    q_bytes = B * S * H * d_qk * 2
     out_bytes = B * S * H * D_V * out_elem + B * S * H * 4
     total = kv_bytes + q_bytes + out_bytes + side
     return {'flops': flops, 'bytes': float(total), 'kv_bytes': float(kv_bytes),
