@@ -141,7 +141,10 @@ const char *mla_status_string(mla_status_t status);
 mla_status_t mla_plan(const mla_problem_t *problem, int32_t num_cus, mla_metadata_t *meta);
 
 /* Bytes of the split-partial workspace a decode call with this plan needs:
- * max_splits * h_q * (512 + 1) float32.  0 if ``meta`` is NULL. */
+ * max_splits * h_q * (512 + 1) float32.  0 if ``meta`` is NULL.  Its contents
+ * are internal to a decode call: with an fp32 output the partials are float32
+ * (the layout mla_combine takes); with a bf16 output they are float16 scaled
+ * per lane by a power of two, with the scales in the unused half. */
 size_t mla_workspace_bytes(const mla_metadata_t *meta);
 
 /* Split-KV tile scheduler.  Writes meta->dev on ``stream`` from

@@ -126,6 +126,12 @@ mla_status_t run_decode(const mla_problem_t* p, bool sparse, const void* q, cons
     a.meta = (const int32_t*)meta->dev;
     a.o_part = (float*)ws;
     a.lse_part = (float*)ws + slots * p->h_q * mla::kDv;
+    // With a bf16 output the split partials travel as scaled float16 (half the
+    // bytes of the partial write and of the combine's read), their scales in
+    // the second half of the float32 partial area; the test hook without the
+    // combine keeps float32 partials.
+    a.part_fp16 = run_combine && p->out_dtype != MLA_OUT_FP32;
+    a.o_exp = (uint32_t*)((char*)ws + slots * p->h_q * mla::kDv * 2);
     a.out = out;
     a.lse = lse;
     a.num_rows = num_rows > 0 ? num_rows : (int64_t)p->num_blocks * kBlock;   // rows a valid index may name
@@ -147,6 +153,8 @@ mla_status_t run_decode(const mla_problem_t* p, bool sparse, const void* q, cons
     mla::CombineArgs c{};
     c.o_part = a.o_part;
     c.lse_part = a.lse_part;
+    c.o_exp = a.o_exp;
+    c.part_fp16 = a.part_fp16;
     c.split_offsets = a.meta + mla::kMetaHeader + mla::kMetaRec * meta->num_partitions;
     c.attn_sink = attn_sink;
     c.out = out;

@@ -36,9 +36,20 @@ __global__ void __launch_bounds__(256) combine_kernel(const CombineArgs a) {
             v[c] = u[c];
             if (k < s1) {
                 lk[c] = a.lse_part[(int64_t)k * H + h];
-                const f32x4* src = (const f32x4*)(a.o_part + ((int64_t)k * H + h) * kDv + lane * 8);
-                u[c] = src[0];
-                v[c] = src[1];
+                if (a.part_fp16) {
+                    // float16 partial scaled by 2^-E; dims lane*8 + 0..3 use byte
+                    // 2 kh, dims + 4..7 byte 2 kh + 1 of the scale word (kh = lane / 32)
+                    typedef __attribute__((__vector_size__(8 * sizeof(_Float16)))) _Float16 f16x8;
+                    const f16x8 x = *(const f16x8*)((const _Float16*)a.o_part + ((int64_t)k * H + h) * kDv + lane * 8);
+                    const uint32_t ew = a.o_exp[(int64_t)k * H + h] >> (16 * (lane >> 5));
+                    const int e0 = (int)(signed char)(ew & 0xff), e1 = (int)(signed char)((ew >> 8) & 0xff);
+                    u[c] = f32x4{ldexpf((float)x[0], e0), ldexpf((float)x[1], e0), ldexpf((float)x[2], e0), ldexpf((float)x[3], e0)};
+                    v[c] = f32x4{ldexpf((float)x[4], e1), ldexpf((float)x[5], e1), ldexpf((float)x[6], e1), ldexpf((float)x[7], e1)};
+                } else {
+                    const f32x4* src = (const f32x4*)(a.o_part + ((int64_t)k * H + h) * kDv + lane * 8);
+                    u[c] = src[0];
+                    v[c] = src[1];
+                }
             }
         }
         float mc = m;

@@ -766,6 +766,25 @@ __global__ void __launch_bounds__(kThreads, 1) decode_kernel(const DecodeArgs a)
             float inv = l_run > 0.f ? 1.f / l_run : 0.f;
             // attention sink: a final output is scaled by exp(lse) / (exp(lse) + exp(sink))
             if (final_out && a.attn_sink && head_ok) inv *= 1.f / (1.f + __expf(a.attn_sink[head] - lse_v));
+            // Split partials in float16 (when the output is bf16): each lane scales
+            // its 128 values by 2^-E, E from the exponent of their largest
+            // magnitude, so they lie in [-1, 1) and cannot overflow; E is stored
+            // as byte 2 kh + half of the head's scale word (the byte of every
+            // dim d with d / 256 = kh and d % 8 / 4 = half).
+            const bool part16 = !final_out && a.part_fp16;
+            int E = 0;
+            if (part16 && head_ok) {
+                float amax = 0.f;
+#pragma unroll
+                for (int dd = 0; dd < 8; ++dd)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) amax = fmaxf(amax, fabsf(acc[dd][r]));
+                amax *= inv;
+                const int be = (int)((__float_as_uint(amax) >> 23) & 0xff);   // biased exponent
+                E = amax > 0.f ? (be == 0 ? -125 : be - 126) : 0;              // amax * 2^-E < 1
+                E = E > 127 ? 127 : E;
+                ((unsigned char*)a.o_exp)[((int64_t)slot * H + head) * 4 + 2 * kh + half] = (unsigned char)(signed char)E;
+            }
             if (head_ok) {
 #pragma unroll
                 for (int dd = 0; dd < 8; ++dd) {
@@ -774,7 +793,12 @@ __global__ void __launch_bounds__(kThreads, 1) decode_kernel(const DecodeArgs a)
                         const int dim = 256 * kh + 32 * dd + 8 * rq + 4 * half;
                         const float v0 = acc[dd][4 * rq + 0] * inv, v1 = acc[dd][4 * rq + 1] * inv;
                         const float v2 = acc[dd][4 * rq + 2] * inv, v3 = acc[dd][4 * rq + 3] * inv;
-                        if (final_out) {
+                        if (part16) {
+                            const int64_t o = ((int64_t)slot * H + head) * kDv + dim;
+                            typedef __attribute__((__vector_size__(4 * sizeof(_Float16)))) _Float16 f16x4;
+                            *(f16x4*)((_Float16*)a.o_part + o) = f16x4{(_Float16)ldexpf(v0, -E), (_Float16)ldexpf(v1, -E),
+                                                                         (_Float16)ldexpf(v2, -E), (_Float16)ldexpf(v3, -E)};
+                        } else if (final_out) {
                             const int64_t o = ((int64_t)j * H + head) * kDv + dim;
                             if (a.out_fp32) {
                                 *(f32x4*)((float*)a.out + o) = f32x4{v0, v1, v2, v3};

@@ -15,8 +15,10 @@ struct DecodeArgs {
     const int32_t* topk_length;  // sparse: [B*S] top-k entries used per query token, or null (all)
     const float* attn_sink;      // [H] per-head sink logits, or null
     const int32_t* meta;         // scheduler metadata (device)
-    float* o_part;               // [max_slots, H, 512]
+    float* o_part;               // [max_slots, H, 512] float32, or float16 when part_fp16
     float* lse_part;             // [max_slots, H]
+    uint32_t* o_exp;             // part_fp16: [max_slots, H] four int8 power-of-two scales per head
+    int part_fp16;               // split partials stored as scaled float16 (see the decode epilogue)
     void* out;                   // [B, S, H, 512]
     float* lse;                  // [B, H, S]
     int64_t num_rows;            // num_blocks * 64
@@ -33,8 +35,10 @@ struct MetaArgs {
 };
 
 struct CombineArgs {
-    const float* o_part;
+    const float* o_part;         // float32, or float16 with o_exp scales when part_fp16
     const float* lse_part;
+    const uint32_t* o_exp;
+    int part_fp16;
     const int32_t* split_offsets;
     const float* attn_sink;      // [H] or null
     void* out;
