@@ -277,6 +277,26 @@ __device__ __forceinline__ void mstep_schedule_all() {
     if constexpr (QK) __builtin_amdgcn_sched_group_barrier(kSchedDsWrite, 4, 0);
 }
 
+// The same order when a tile-copy piece follows each of the first
+// kMstepPieces operations.  Each piece (inline assembly) is fenced by
+// scheduling barriers, without which the MFMAs, having no memory operands,
+// drift across it and the reads lose their lookahead; the pins are then given
+// region by region.  Region 0 holds the first reads and operation 0, region
+// i < kMstepPieces operation i, the last region the remaining operations and
+// the score stores.
+constexpr int kMstepPieces = 4;   // pieces of each tile copy issued in the MFMA step (of nine)
+template <int I>
+__device__ __forceinline__ void mstep_schedule_region() {
+    if constexpr (I == 0)
+        __builtin_amdgcn_sched_group_barrier(kSchedDsRead, mstep_first_reads<0, kMstepLookahead>(), 0);
+    mstep_schedule<I, I + 1>();
+}
+template <int I1>
+__device__ __forceinline__ void mstep_schedule_tail() {
+    mstep_schedule<kMstepPieces, I1>();
+    __builtin_amdgcn_sched_group_barrier(kSchedDsWrite, 4, 0);
+}
+
 // A tile copy to be issued piecewise: buffer resource, sparse row id, lane
 // source offset and LDS address of the wave's first piece.
 struct FillCtx {
@@ -511,23 +531,69 @@ __global__ void __launch_bounds__(kThreads, 1) decode_kernel(const DecodeArgs a)
         // M(ns) is the last PV alone.  Group 0 runs M(t), V(t) in steps 2t,
         // 2t+1; group 1 runs V(t-1), M(t), so on every SIMD one wave issues
         // MFMAs while the other runs the softmax.  Tile t is read in steps
-        // 2t..2t+3.  Group 1 copies tile t+1 into the buffer of tile t-2 at the
-        // start of step 2t; every wave waits for its copies at the end of step
+        // 2t..2t+3.  Both groups copy parts of tile t+1 into the buffer of tile
+        // t-2 during step 2t; every wave waits for its copies at the end of step
         // 2t+1.  Every step ends with a workgroup barrier.  The
         // group is a compile-time constant so that each wave's step sequence is
         // straight-line code.
         f32x16 s = {};
         bf16x8 p0 = {}, p1 = {};
 
+        // Copy of tile t+1 into the buffer of tile t-2 in step 2t, as nine 1-KiB
+        // pieces per wave (wave w of a group copies the pieces w + 4i).  Group 0
+        // issues pieces 0..kMstepPieces-1, one after each of its first MFMAs;
+        // group 1 issues the rest spread over its softmax step.  Each issuing
+        // cost lands on a wave with slack, and group 0's share starts early.
+        // In step 0 group 1, which has no other work, issues all nine.
+        // With no tile left to copy the pieces still run, on an empty buffer
+        // range: they write zeros into the buffer of tile t-2, which no step
+        // reads any more.  Keeping them unconditional keeps the softmax step one
+        // basic block (a branch around each piece makes the compiler wait for
+        // every outstanding copy before the next one).
+        auto fill_prepare = [&](int t) __attribute__((always_inline)) -> FillCtx {
+            FillCtx f{true, {0, 0, 0, 0}, nullptr, 0, 0};
+            const int g = g0 + t + 1;
+            const int w = wave & 3;
+            const bool live = t + 1 < ns;
+            f.l0 = (int)(size_t)(lds_void_t*)&sm.tile[0][0] + opaque_tile_offset((t + 1) % kNBuf) + 1024 * w;
+            if (SPARSE) {
+                f.src = bf16_row_addr(kv, live ? sm.rows[(t + 1) & 3][ftok] : -1, fcol + 32 * w);
+            } else if (!live) {
+                f.rs = buffer_rsrc(kv, 0, 0);
+                f.vo = fbase + 32 * w;
+            } else {
+                const bool ok = page_ok(pg1, a.num_rows);
+                int nvalid = min(nslots - g * kSubTok, kSubTok);
+                if (!ok || nvalid < 0) nvalid = 0;
+                f.rs = buffer_rsrc(kv + (ok ? (int64_t)pg1 * kTileBytes + (g & 1) * kSubBytes : 0), 0,
+                                   nvalid * kRowBytes);
+                f.vo = fbase + 32 * w;
+            }
+            return f;
+        };
+        auto fill_piece = [&](const FillCtx& f, auto i_c) __attribute__((always_inline)) {
+            constexpr int i = decltype(i_c)::value;
+            if (f.on) {
+                if (SPARSE) dma_global_x4<128 * i>(f.src, f.l0 + 4096 * i);
+                else dma_raw_x4<128 * i>(f.rs, f.vo, f.l0 + 4096 * i);
+            }
+        };
+        const FillCtx nofill{false, {0, 0, 0, 0}, nullptr, 0, 0};
+        // the pieces group 1 issues in its softmax step
+        auto fill_soft = [&](const FillCtx& f, auto i_c) __attribute__((always_inline)) {
+            if constexpr (decltype(i_c)::value >= kMstepPieces) fill_piece(f, i_c);
+        };
         // MFMA step body: PV(t-1) (16 MFMAs) then QK(t) (18 MFMAs), as one
         // sequence of operations whose LDS operands are fetched kMstepLookahead
         // ahead.  Operation i < 16 is PV k-step i/8 for output block i%8; operation 16 + k is
         // QK k-step k (k < 16 latent dims of this half, then two RoPE k-steps
         // whose Q fragment also comes from LDS).  P and S are never live
         // together.
-        auto mstep = [&](int t, auto pv_c, auto qk_c) __attribute__((always_inline)) {
+        auto mstep = [&](int t, auto pv_c, auto qk_c, const FillCtx& fc, auto fill_c) __attribute__((always_inline)) {
             constexpr bool DO_PV = decltype(pv_c)::value != 0;
             constexpr bool DO_QK = decltype(qk_c)::value != 0;
+            // copy pieces after the first MFMAs (full steady-state step only)
+            constexpr bool FILL = decltype(fill_c)::value != 0 && DO_PV && DO_QK && !FP8;
             constexpr int I0 = DO_PV ? 0 : 16;
             constexpr int I1 = DO_QK ? (D512 ? 32 : 34) : 16;   // the 512-wide head has no RoPE steps
             const unsigned char* Tp = sm.tile[0] + opaque_tile_offset((t + kNBuf - 1) % kNBuf) + 16384 * kh;  // t-1
@@ -566,6 +632,12 @@ __global__ void __launch_bounds__(kThreads, 1) decode_kernel(const DecodeArgs a)
                     } else {
                         s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(opA[r], opB[r], s, 0, 0, 0);
                     }
+                    if constexpr (FILL && i < kMstepPieces) {
+                        mstep_schedule_region<i>();
+                        __builtin_amdgcn_sched_barrier(0);
+                        fill_piece(fc, IntC<i>{});
+                        __builtin_amdgcn_sched_barrier(0);
+                    }
                 }
             });
             if (DO_QK) {
@@ -573,45 +645,9 @@ __global__ void __launch_bounds__(kThreads, 1) decode_kernel(const DecodeArgs a)
                 for (int i = 0; i < 4; ++i)
                     sm.xs[hb][kh][i][lane] = f32x4{s[4 * i], s[4 * i + 1], s[4 * i + 2], s[4 * i + 3]};
             }
-            mstep_schedule_all<I0, I1, DO_QK>();
+            if constexpr (FILL) mstep_schedule_tail<I1>();
+            else mstep_schedule_all<I0, I1, DO_QK>();
         };
-        // Copy of tile t+1 into the buffer of tile t-2, issued by group 1 during
-        // its softmax step 2t: wave 4 + w issues the nine 1-KiB pieces w + 4i,
-        // spread over the softmax so that the copies never queue up at once.
-        // With no tile left to copy the pieces still run, on an empty buffer
-        // range: they write zeros into the buffer of tile t-2, which no step
-        // reads any more.  Keeping them unconditional keeps the softmax step one
-        // basic block (a branch around each piece makes the compiler wait for
-        // every outstanding copy before the next one).
-        auto fill_prepare = [&](int t) __attribute__((always_inline)) -> FillCtx {
-            FillCtx f{true, {0, 0, 0, 0}, nullptr, 0, 0};
-            const int g = g0 + t + 1;
-            const int w = wave - 4;
-            const bool live = t + 1 < ns;
-            f.l0 = (int)(size_t)(lds_void_t*)&sm.tile[0][0] + opaque_tile_offset((t + 1) % kNBuf) + 1024 * w;
-            if (SPARSE) {
-                f.src = bf16_row_addr(kv, live ? sm.rows[(t + 1) & 3][ftok] : -1, fcol + 32 * w);
-            } else if (!live) {
-                f.rs = buffer_rsrc(kv, 0, 0);
-                f.vo = fbase + 32 * w;
-            } else {
-                const bool ok = page_ok(pg1, a.num_rows);
-                int nvalid = min(nslots - g * kSubTok, kSubTok);
-                if (!ok || nvalid < 0) nvalid = 0;
-                f.rs = buffer_rsrc(kv + (ok ? (int64_t)pg1 * kTileBytes + (g & 1) * kSubBytes : 0), 0,
-                                   nvalid * kRowBytes);
-                f.vo = fbase + 32 * w;
-            }
-            return f;
-        };
-        auto fill_piece = [&](const FillCtx& f, auto i_c) __attribute__((always_inline)) {
-            constexpr int i = decltype(i_c)::value;
-            if (f.on) {
-                if (SPARSE) dma_global_x4<128 * i>(f.src, f.l0 + 4096 * i);
-                else dma_raw_x4<128 * i>(f.rs, f.vo, f.l0 + 4096 * i);
-            }
-        };
-        const FillCtx nofill{false, {0, 0, 0, 0}, nullptr, 0, 0};
         // full scores, mask, exact online softmax.  Register r holds token
         // 8(r/4) + 4*half + r%4 of the tile.  Scores stay unscaled; c > 0 is
         // folded into the exponent.
@@ -630,8 +666,8 @@ __global__ void __launch_bounds__(kThreads, 1) decode_kernel(const DecodeArgs a)
             f32x4 xo[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i) xo[i] = sm.xs[hb][kh ^ 1][i][lane];
-            fill_piece(fc, IntC<0>{});
-            fill_piece(fc, IntC<1>{});
+            fill_soft(fc, IntC<0>{});
+            fill_soft(fc, IntC<1>{});
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
 #pragma unroll
@@ -653,8 +689,8 @@ __global__ void __launch_bounds__(kThreads, 1) decode_kernel(const DecodeArgs a)
 #pragma unroll
             for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[r]);
             mx = wave_max_pair(mx);
-            fill_piece(fc, IntC<2>{});
-            fill_piece(fc, IntC<3>{});
+            fill_soft(fc, IntC<2>{});
+            fill_soft(fc, IntC<3>{});
             // Running max: raised to the tile max only when that exceeds it by
             // more than tau in log2 units (tau = 0: whenever it is larger,
             // the exact running max).  From -inf any finite max is taken.
@@ -667,9 +703,9 @@ __global__ void __launch_bounds__(kThreads, 1) decode_kernel(const DecodeArgs a)
                 constexpr int r = decltype(r_c)::value;
                 s[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c, -cm));
                 psum += s[r];
-                if constexpr (r == 5) fill_piece(fc, IntC<4>{});
-                if constexpr (r == 10) fill_piece(fc, IntC<5>{});
-                if constexpr (r == 15) fill_piece(fc, IntC<6>{});
+                if constexpr (r == 5) fill_soft(fc, IntC<4>{});
+                if constexpr (r == 10) fill_soft(fc, IntC<5>{});
+                if constexpr (r == 15) fill_soft(fc, IntC<6>{});
             });
             psum = wave_sum_pair(psum);
             // rescale O (lane l holds head l%32); skipped when no head's max rose.
@@ -681,12 +717,12 @@ __global__ void __launch_bounds__(kThreads, 1) decode_kernel(const DecodeArgs a)
 #pragma unroll
                     for (int r = 0; r < 16; ++r) acc[dd][r] *= alpha;
             }
-            fill_piece(fc, IntC<7>{});
+            fill_soft(fc, IntC<7>{});
             l_run = l_run * alpha + psum;
             m_run = m_new;
 #pragma unroll
             for (int e = 0; e < 8; ++e) { p0[e] = (__bf16)s[e]; p1[e] = (__bf16)s[8 + e]; }
-            fill_piece(fc, IntC<8>{});
+            fill_soft(fc, IntC<8>{});
             __builtin_amdgcn_s_setprio(0);
         };
         // step 2t: FP8 tile t+1 to registers; sparse row ids of tile t+2
@@ -708,7 +744,7 @@ __global__ void __launch_bounds__(kThreads, 1) decode_kernel(const DecodeArgs a)
                     __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's copies of tile t+1
                     fp8_dequant(t + 1);
                 }
-                else if (grp == 1) __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): group 1's tile copies
+                else if (t > 0 || grp == 1) __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's tile copies
             }
             if (!SPARSE) {
                 if (((g0 + t + 3) >> 1) - pt_base >= 64) load_pages((g0 + t) >> 1);
@@ -725,7 +761,7 @@ __global__ void __launch_bounds__(kThreads, 1) decode_kernel(const DecodeArgs a)
             // steps 0, 1
             int nr = step_even_begin(0);
             if (G == 0) {
-                mstep(0, no, yes);
+                mstep(0, no, yes, nofill, no);
             } else {
                 if (!FP8) {
                     const FillCtx fc = fill_prepare(0);
@@ -734,23 +770,23 @@ __global__ void __launch_bounds__(kThreads, 1) decode_kernel(const DecodeArgs a)
             }
             step_even_end(0, nr);
             if (G == 0) soft(0, nofill, no);
-            else mstep(0, no, yes);
+            else mstep(0, no, yes, nofill, no);
             step_odd_end(0);
             // steady state: steps 2t, 2t+1
             for (int t = 1; t < ns; ++t) {
                 nr = step_even_begin(t);
-                if (G == 0) mstep(t, yes, yes);
+                if (G == 0) mstep(t, yes, yes, fill_prepare(t), yes);
                 else soft(t - 1, fill_prepare(t), yes);
                 step_even_end(t, nr);
                 if (G == 0) soft(t, nofill, no);
-                else mstep(t, yes, yes);
+                else mstep(t, yes, yes, nofill, no);
                 step_odd_end(t);
             }
             // drain: steps 2ns, 2ns+1 (the last tile's PV)
-            if (G == 0) mstep(ns, yes, no);
+            if (G == 0) mstep(ns, yes, no, nofill, no);
             else soft(ns - 1, nofill, no);
             lds_barrier();
-            if (G == 1) mstep(ns, yes, no);
+            if (G == 1) mstep(ns, yes, no, nofill, no);
             lds_barrier();
         };
         if (grp == 0) run(IntC<0>{});
