@@ -118,6 +118,25 @@ def cpu_baseline(w, flops):
                       f"fp64 numpy, {dt:.1f} s in total"}
 
 
+def _warmup(fn, count, stream, budget_s=0.06):
+    """Run ``count`` untimed steps, or (count None) steps until ``budget_s`` of
+    work has run, at least 10; returns the number run."""
+    import time
+    import torch
+    if count is not None:
+        for _ in range(count):
+            fn()
+        torch.cuda.synchronize()
+        return count
+    n, t0 = 0, time.perf_counter()
+    while n < 10 or time.perf_counter() - t0 < budget_s:
+        for _ in range(5):
+            fn()
+        n += 5
+        torch.cuda.synchronize()
+    return n
+
+
 def _timed(fn, steps, stream):
     import torch
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -150,8 +169,7 @@ def bench_prefill(args):
         dec.metadata(None, stream)
         mla.sparse_prefill_fwd(p, s_kv, w.q, w.kv, w.indices, dec.meta, dec.workspace, dec.out, dec.lse, stream)
 
-    for _ in range(args.warmup):
-        step()
+    args.warmup = _warmup(step, args.warmup, stream)
     ms_step = _timed(step, args.steps, stream)
     ms_kernel = _timed(lambda: dec.decode_partial(w.q, w.kv, None, None, w.indices, stream), args.steps, stream)
     kern_tflops = flops / (ms_kernel * 1e-3) / 1e12
@@ -181,7 +199,12 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    # Default: untimed steps until about 60 ms of work has run (at least 10).
+    # The GPU clock ramps up over the first ~10-20 ms of sustained work, so the
+    # timed steps then see the steady state a serving loop runs at; a fixed
+    # count would either stop inside the ramp (short steps) or heat the chip
+    # for seconds first (long steps).
+    ap.add_argument("--warmup", type=int, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--workload", default="dense_b64_s4096",
                     choices=["dense_b64_s4096", "fp8_sparse_topk2048", "fp8_sparse_topk32768", "sparse_prefill",
@@ -231,9 +254,7 @@ def main():
         dec.metadata(seqlens, stream)
         dec.decode(w.q, w.kv, w.block_table, w.cache_seqlens, w.indices, stream)
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
+    args.warmup = _warmup(step, args.warmup, stream)
     # timed region: exactly K whole steps
     ms_step = _timed(step, args.steps, stream)
 
