@@ -49,7 +49,7 @@ import math
 import numpy as np
 
 from .numerics import bf16_bits_to_f64
-from .fp8cache import dequant_records, dequant_records_v41, RECORD_BYTES, V41_RECORD_BYTES
+from .fp8cache import dequant_records, dequant_records_v41, dequant_records_fp4, RECORD_BYTES, V41_RECORD_BYTES
 from .sched import visible_len
 
 D_QK = 576
@@ -163,7 +163,7 @@ def merge_partials(o_parts, lse_parts):
 
 def kv_values(kv, rows, kv_format):
     """Gather physical cache rows and decode them to float64 [n, 576] (or
-    [n, 512] for the 528-byte records of the 512-wide head)."""
+    [n, 512] for the 528- and 288-byte records of the 512-wide head)."""
     rows = np.asarray(rows, dtype=np.int64)
     if kv_format == 'bf16':
         return bf16_bits_to_f64(kv[rows])
@@ -173,6 +173,8 @@ def kv_values(kv, rows, kv_format):
     if kv_format == 'fp8_528':
         assert kv.shape[-1] == V41_RECORD_BYTES
         return dequant_records_v41(kv[rows])
+    if kv_format == 'fp4_288':
+        return dequant_records_fp4(kv[rows])
     raise ValueError(kv_format)
 
 
@@ -230,7 +232,7 @@ def decode(q_bits, kv, softmax_scale, *, block_table=None, cache_seqlens=None,
     """
     q_bits = np.asarray(q_bits)
     B, S, H, D = q_bits.shape
-    assert D == (512 if kv_format == 'fp8_528' else D_QK)
+    assert D == (512 if kv_format in ('fp8_528', 'fp4_288') else D_QK)
     num_rows = kv.shape[0]
     out = np.full((B, S, H, D_V), np.nan)
     lse = np.full((B, H, S), np.nan)

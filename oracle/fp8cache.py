@@ -89,3 +89,46 @@ def dequant_records_v41(rec):
     scales = e8m0_decode(flat[:, V41_DIM:])                      # [n, 16]
     out = vals * np.repeat(scales, V41_GROUP, axis=1)
     return out.reshape(lead + (V41_DIM,))
+
+
+# --------------------------------------------------------------------------
+# The 288-byte FP4 record of the same 512-wide head (FlashMLA README copy,
+# "FP8 / FP4 KV Cache Format"): per token 256 bytes holding 512 e2m1 values,
+# two per byte with the even-indexed value in the low nibble, then 32
+# float8_e4m3 scales, one for every 16 consecutive values.  K and V are both
+# the 512 values.
+#
+# Readings: e2m1 is the OCP microscaling FP4 element (1 sign bit, 2 exponent
+# bits with bias 1, 1 mantissa bit, no infinities or NaN): magnitudes 0, 0.5,
+# 1, 1.5, 2, 3, 4, 6.  The dequantised value e2m1 * e4m3 has at most five
+# significant bits and lies in [2^-10, 2688], so it is exact in float64 and in
+# bfloat16 and is returned unrounded; an e4m3 NaN scale (0x7F/0xFF) gives NaN.
+
+FP4_RECORD_BYTES = 288
+FP4_DIM = 512
+FP4_GROUP = 16
+
+
+def e2m1_decode(codes):
+    """4-bit e2m1 codes (0..15) -> float64 values."""
+    c = np.asarray(codes, dtype=np.int64)
+    sign = np.where(c & 8, -1.0, 1.0)
+    e = (c >> 1) & 3
+    m = (c & 1).astype(np.float64)
+    mag = np.where(e == 0, 0.5 * m, np.ldexp(1.0 + 0.5 * m, (e - 1).astype(np.int32)))
+    return sign * mag
+
+
+def dequant_records_fp4(rec):
+    """uint8 records [..., 288] -> float64 K (= V) values [..., 512]."""
+    rec = np.asarray(rec, dtype=np.uint8)
+    assert rec.shape[-1] == FP4_RECORD_BYTES
+    lead = rec.shape[:-1]
+    flat = np.ascontiguousarray(rec.reshape(-1, FP4_RECORD_BYTES))
+    packed = flat[:, :FP4_DIM // 2].astype(np.int64)
+    codes = np.empty((flat.shape[0], FP4_DIM), dtype=np.int64)
+    codes[:, 0::2] = packed & 0xF          # even index: low nibble
+    codes[:, 1::2] = packed >> 4
+    scales = e4m3fn_decode(flat[:, FP4_DIM // 2:])                 # [n, 32]
+    out = e2m1_decode(codes) * np.repeat(scales, FP4_GROUP, axis=1)
+    return out.reshape(lead + (FP4_DIM,))

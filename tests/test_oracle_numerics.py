@@ -118,3 +118,73 @@ def test_v41_decode_is_attention_over_the_dequantised_rows():
         p = np.exp(s - m)
         assert np.max(np.abs(out[b, 0] - (p @ K) / p.sum(axis=1, keepdims=True))) < 1e-12
         assert np.max(np.abs(lse[b, :, 0] - (m[:, 0] + np.log(p.sum(axis=1))))) < 1e-12
+
+
+# ---------------------------------------------------------------- 288-byte FP4 records
+
+def test_e2m1_all_codes_closed_form():
+    # the OCP e2m1 element: magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6, bit 3 the sign
+    want = [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0, -0.0, -0.5, -1.0, -1.5, -2.0, -3.0, -4.0, -6.0]
+    got = F8.e2m1_decode(np.arange(16))
+    assert np.array_equal(got, np.array(want)) and np.array_equal(np.signbit(got), np.signbit(np.array(want)))
+
+
+def test_fp4_record_layout_matches_pages():
+    # 512 e2m1 values two per byte, then one e4m3 scale for every 16 values: 256 + 32 bytes
+    assert F8.FP4_RECORD_BYTES == 512 // 2 + (512 // 16) * 1 == 288
+
+
+def test_fp4_nibble_order_and_group_scales():
+    """Even-indexed values sit in the low nibble; scale byte k covers values 16k..16k+15."""
+    rec = np.zeros(288, dtype=np.uint8)
+    rec[0] = 0x72                     # values 0, 1 = codes 2, 7 = 1.0, 6.0
+    rec[1] = 0xF9                     # values 2, 3 = codes 9, 15 = -0.5, -6.0
+    rec[8] = 0x35                     # values 16, 17 = codes 5, 3 = 3.0, 1.5
+    rec[256:] = 0x38                  # e4m3 1.0
+    rec[257] = 0x40                   # e4m3 2.0 for values 16..31
+    rec[258] = 0x7F                   # e4m3 NaN for values 32..47
+    v = F8.dequant_records_fp4(rec)
+    assert v.shape == (512,)
+    assert list(v[:4]) == [1.0, 6.0, -0.5, -6.0]
+    assert list(v[16:18]) == [6.0, 3.0]
+    assert np.all(np.isnan(v[32:48])) and np.all(v[48:] == 0.0) and np.all(v[4:16] == 0.0)
+
+
+def test_fp4_dequant_against_torch_scales_and_table():
+    """Dequantised values equal a table lookup of each nibble times torch's
+    float8_e4m3fn decode of the group scale, and stay within 1.5 scale units
+    of the encoded float32 values."""
+    from workloads.gen import encode_fp4_records
+    g = torch.Generator().manual_seed(5)
+    x = torch.randn((64, 512), generator=g) * torch.exp(torch.randn((64, 1), generator=g))
+    rec = encode_fp4_records(x).numpy()
+    got = F8.dequant_records_fp4(rec)
+    table = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0, -0.0, -0.5, -1.0, -1.5, -2.0, -3.0, -4.0, -6.0])
+    lo, hi = rec[:, :256] & 0xF, rec[:, :256] >> 4
+    codes = np.stack([lo, hi], axis=-1).reshape(64, 512)
+    scales = torch.from_numpy(rec[:, 256:].copy()).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    want = table[codes] * np.repeat(scales, 16, axis=1)
+    assert np.array_equal(got, want)
+    s = np.repeat(scales, 16, axis=1)
+    assert np.all(np.abs(got - x.double().numpy()) <= 1.5 * s)
+
+
+def test_fp4_decode_is_attention_over_the_dequantised_rows():
+    """The oracle's decode over 288-byte records equals the plain two-pass
+    attention over the dequantised 512-wide rows, with V = K."""
+    from oracle import attention as A
+    from workloads import make_fp4_sparse
+    w = make_fp4_sparse(2, 1, 4, pool_tokens_per_seq=256, topk=40, invalid_frac=0.1, seed=9)
+    q = w.q.contiguous().view(torch.int16).numpy().view(np.uint16)
+    kv = w.kv.numpy().reshape(-1, 288)
+    idx = w.indices.numpy()
+    out, lse = A.decode(q, kv, w.softmax_scale, indices=idx, kv_format='fp4_288')
+    for b in range(2):
+        rows = idx[b, 0][idx[b, 0] >= 0]
+        K = F8.dequant_records_fp4(kv[rows])
+        qh = Nm.bf16_bits_to_f64(q[b, 0])
+        s = w.softmax_scale * qh @ K.T
+        m = s.max(axis=1, keepdims=True)
+        p = np.exp(s - m)
+        assert np.max(np.abs(out[b, 0] - (p @ K) / p.sum(axis=1, keepdims=True))) < 1e-12
+        assert np.max(np.abs(lse[b, :, 0] - (m[:, 0] + np.log(p.sum(axis=1))))) < 1e-12

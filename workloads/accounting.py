@@ -32,8 +32,8 @@ def visible(L, s_q, i, causal):
 def flops_and_bytes(w):
     """Algorithmic FLOPs and HBM bytes of one decode call on workload ``w``."""
     B, S, H = w.batch, w.s_q, w.h_q
-    row_bytes = {'bf16': 1152, 'fp8': 656, 'fp8_528': 528}[w.kv_format]
-    d_qk = 512 if w.kv_format == 'fp8_528' else D_QK
+    row_bytes = {'bf16': 1152, 'fp8': 656, 'fp8_528': 528, 'fp4_288': 288}[w.kv_format]
+    d_qk = 512 if w.kv_format in ('fp8_528', 'fp4_288') else D_QK
     out_elem = 2 if w.out_dtype == 'bf16' else 4
     if w.topk:
         idx = w.indices.to('cpu').to(torch.int64)

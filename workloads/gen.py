@@ -219,6 +219,7 @@ def make_sparse(batch, s_q, h_q, *, pool_tokens_per_seq, topk, invalid_frac=0.05
 
 
 V41_RECORD = 528
+FP4_RECORD = 288
 
 
 def encode_v41_records(x):
@@ -254,6 +255,49 @@ def make_v41_sparse(batch, s_q, h_q, *, pool_tokens_per_seq, topk, invalid_frac=
         kv[s:e] = encode_v41_records(x).view(e - s, BLOCK, 1, V41_RECORD)
     w.kv = kv
     w.kv_format = 'fp8_528'
+    w.q = _randn_bf16((batch, s_q, h_q, 512), g, device, chunk_rows=64)
+    w.softmax_scale = 1.0 / math.sqrt(512)
+    return w
+
+
+E2M1_MAGNITUDES = (0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0)   # codes 0..7 (bit 3 is the sign)
+
+
+def encode_fp4_records(x):
+    """float32 [n, 512] -> uint8 [n, 288]: per group of 16 values the scale float8_e4m3fn(amax / 6) (torch's
+    round-to-nearest cast; 1 for an all-zero group), each value x / scale rounded to the nearest e2m1
+    magnitude (ties to the smaller code) with its sign, two codes per byte with the even index in the low
+    nibble, then the 32 scale bytes."""
+    n = x.shape[0]
+    g = x.view(n, 32, 16)
+    amax = g.abs().amax(dim=-1)
+    scale = torch.where(amax > 0, amax / 6.0, torch.ones_like(amax)).to(torch.float8_e4m3fn)
+    s = scale.to(torch.float32)
+    s = torch.where(s > 0, s, torch.ones_like(s))
+    y = (g / s[..., None]).reshape(n, 512)
+    mags = torch.tensor(E2M1_MAGNITUDES, device=x.device)
+    code = (y.abs()[..., None] - mags).abs().argmin(dim=-1)          # first minimum: ties to the smaller code
+    code = code + 8 * ((y < 0) & (code > 0)).to(code.dtype)
+    code = code.to(torch.uint8)
+    packed = code[:, 0::2] | (code[:, 1::2] << 4)
+    return torch.cat([packed, scale.view(torch.uint8)], dim=1)
+
+
+def make_fp4_sparse(batch, s_q, h_q, *, pool_tokens_per_seq, topk, invalid_frac=0.0, seed=0, device='cpu',
+                    name='fp4_sparse'):
+    """Top-k decode inputs over the 288-byte FP4 records of the 512-wide head: q is [batch, s_q, h_q, 512];
+    cache values N(0, 1) encoded by ``encode_fp4_records``; indices as for ``make_sparse``."""
+    w = make_sparse(batch, s_q, h_q, pool_tokens_per_seq=pool_tokens_per_seq, topk=topk, invalid_frac=invalid_frac,
+                    seed=seed, device=device, name=name)
+    nb = w.num_blocks
+    g = _gen(device, seed + 130363)
+    kv = torch.empty((nb, BLOCK, 1, FP4_RECORD), dtype=torch.uint8, device=device)
+    for s in range(0, nb, 256):
+        e = min(nb, s + 256)
+        x = torch.randn(((e - s) * BLOCK, 512), generator=g, device=device)
+        kv[s:e] = encode_fp4_records(x).view(e - s, BLOCK, 1, FP4_RECORD)
+    w.kv = kv
+    w.kv_format = 'fp4_288'
     w.q = _randn_bf16((batch, s_q, h_q, 512), g, device, chunk_rows=64)
     w.softmax_scale = 1.0 / math.sqrt(512)
     return w
