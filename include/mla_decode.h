@@ -66,12 +66,18 @@ typedef enum {
      * the README copy's newer model, RoPE dims quantised too (README copy, "FP8 /
      * FP4 KV Cache Format").  d_qk = d_v = 512 (K and V are the same 512
      * values), q is [batch, s_q, h_q, 512]; top-k sparse problems only. */
-    MLA_KV_FP8_528 = 2
+    MLA_KV_FP8_528 = 2,
+    /* 256 bytes of e2m1 pairs (512 values, the even-indexed one in the low
+     * nibble) | 32 float8_e4m3fn scales (1 per 16 values): the FP4 record of
+     * the same 512-wide head (README copy, "FP8 / FP4 KV Cache Format", where it
+     * serves as the extra cache beside a 528-byte one; here a sparse cache
+     * format of its own).  Same shapes and restrictions as MLA_KV_FP8_528. */
+    MLA_KV_FP4_288 = 3
 } mla_kv_format_t;
 
 typedef enum { MLA_OUT_BF16 = 0, MLA_OUT_FP32 = 1 } mla_out_dtype_t;
 
-/* Problem shape.  Supported: h_kv = 1, d_qk = 576 (512 for MLA_KV_FP8_528), d_v = 512, block_size = 64
+/* Problem shape.  Supported: h_kv = 1, d_qk = 576 (512 for MLA_KV_FP8_528 and MLA_KV_FP4_288), d_v = 512, block_size = 64
  * (FlashMLA README: the key cache has one head; d_v can only be 512).  Tensor
  * layouts:
  *   q            [batch, s_q, h_q, 576]              bfloat16

@@ -50,10 +50,11 @@ def abi_version():
 def make_problem(batch, s_q, h_q, num_blocks, max_blocks_per_seq=0, *, topk=0, causal=False, kv_format="bf16",
                  out_dtype="bf16", softmax_scale=None, rescale_threshold=0.0):
     p = Problem()
-    d_qk = 512 if kv_format == "fp8_528" else 576
+    d_qk = 512 if kv_format in ("fp8_528", "fp4_288") else 576
     p.batch, p.s_q, p.h_q, p.h_kv, p.d_qk, p.d_v, p.block_size = batch, s_q, h_q, 1, d_qk, 512, 64
     p.num_blocks, p.max_blocks_per_seq, p.topk, p.causal = num_blocks, max_blocks_per_seq, topk, int(bool(causal))
-    p.kv_format = {"bf16": _lib.KV_BF16_576, "fp8": _lib.KV_FP8_656, "fp8_528": _lib.KV_FP8_528}[kv_format]
+    p.kv_format = {"bf16": _lib.KV_BF16_576, "fp8": _lib.KV_FP8_656, "fp8_528": _lib.KV_FP8_528,
+                   "fp4_288": _lib.KV_FP4_288}[kv_format]
     p.out_dtype = {"bf16": _lib.OUT_BF16, "fp32": _lib.OUT_FP32}[out_dtype]
     p.softmax_scale = 1.0 / math.sqrt(576) if softmax_scale is None else float(softmax_scale)
     p.rescale_threshold = float(rescale_threshold)
@@ -169,7 +170,7 @@ def sparse_prefill(q, kv, indices, sm_scale=None, topk_length=None, attn_sink=No
     schedules and allocates the outputs and workspace with torch on q's device, then runs the library."""
     s_q, h_q = int(q.shape[0]), int(q.shape[1])
     s_kv, topk = int(kv.shape[0]), int(indices.shape[-1])
-    fmt = "bf16" if kv.dtype != torch.uint8 else ("fp8_528" if int(kv.shape[-1]) == 528 else "fp8")
+    fmt = "bf16" if kv.dtype != torch.uint8 else {528: "fp8_528", 288: "fp4_288"}.get(int(kv.shape[-1]), "fp8")
     p = make_problem(1, s_q, h_q, (s_kv + 63) // 64, topk=topk, kv_format=fmt, out_dtype=out_dtype,
                      softmax_scale=sm_scale, rescale_threshold=rescale_threshold)
     m = plan(p, num_cus)

@@ -17,6 +17,7 @@ STATUS_NAMES = {0: "MLA_OK", 1: "MLA_ERR_INVALID_ARG", 2: "MLA_ERR_UNSUPPORTED",
 KV_BF16_576 = 0
 KV_FP8_656 = 1
 KV_FP8_528 = 2
+KV_FP4_288 = 3
 OUT_BF16 = 0
 OUT_FP32 = 1
 

@@ -41,16 +41,18 @@ mla_status_t validate(const mla_problem_t* p) {
     if (p->batch < 1 || p->s_q < 1 || p->h_q < 1 || p->num_blocks < 1) return MLA_ERR_INVALID_ARG;
     if (p->topk < 0 || p->max_blocks_per_seq < 0) return MLA_ERR_INVALID_ARG;
     if (p->causal != 0 && p->causal != 1) return MLA_ERR_INVALID_ARG;
-    if (p->kv_format != MLA_KV_BF16_576 && p->kv_format != MLA_KV_FP8_656 && p->kv_format != MLA_KV_FP8_528)
+    if (p->kv_format != MLA_KV_BF16_576 && p->kv_format != MLA_KV_FP8_656 && p->kv_format != MLA_KV_FP8_528 &&
+        p->kv_format != MLA_KV_FP4_288)
         return MLA_ERR_INVALID_ARG;
     if (p->out_dtype != MLA_OUT_BF16 && p->out_dtype != MLA_OUT_FP32) return MLA_ERR_INVALID_ARG;
     if (!std::isfinite(p->softmax_scale) || !(p->softmax_scale > 0.f)) return MLA_ERR_INVALID_ARG;
     if (!(p->rescale_threshold >= 0.f && p->rescale_threshold <= 30.f)) return MLA_ERR_INVALID_ARG;
-    // the 528-byte records carry the 512-wide head (K = V), read through top-k indices
-    const int d_qk = p->kv_format == MLA_KV_FP8_528 ? 512 : mla::kDqk;
+    // the 528- and 288-byte records carry the 512-wide head (K = V), read through top-k indices
+    const bool d512 = p->kv_format == MLA_KV_FP8_528 || p->kv_format == MLA_KV_FP4_288;
+    const int d_qk = d512 ? 512 : mla::kDqk;
     if (p->h_kv != 1 || p->d_qk != d_qk || p->d_v != mla::kDv || p->block_size != kBlock)
         return MLA_ERR_UNSUPPORTED;
-    if (p->kv_format == MLA_KV_FP8_528 && p->topk < 1) return MLA_ERR_UNSUPPORTED;
+    if (d512 && p->topk < 1) return MLA_ERR_UNSUPPORTED;
     if (p->topk == 0 && p->max_blocks_per_seq < 1) return MLA_ERR_INVALID_ARG;
     if (p->topk > 0 && p->causal) return MLA_ERR_UNSUPPORTED;
     const int64_t items = (int64_t)p->batch * p->s_q;

@@ -197,6 +197,34 @@ __device__ __forceinline__ float e8m0_scale(unsigned e) {
 __device__ __forceinline__ int fp8_code_token(int l) { return (l & 31) ^ (8 + 4 * (l >> 5)); }   // c = 4p+2
 __device__ __forceinline__ int fp8_rope_token(int l, int w) { return (l & 31) ^ (4 * (l >> 5) + 8 * (w & 1)); }
 
+// 288-byte FP4 record: wave w copies the code chunks of parts 2w, 2w+1 (16 B,
+// 32 e2m1 values each) into columns 8w+3 and 8w+4 with one instruction, so
+// lane l reads token (l & 31) ^ col_xor(8w + 3 + (l >> 5)).
+__device__ __forceinline__ int fp4_code_token(int l) { return (l & 31) ^ ((l >> 5) ? 0 : 12); }
+
+// e2m1 pairs -> fp32 (exact: the conversion with scale 1, the even-indexed
+// value from the low nibble), x the e4m3 scale of its group of 16 (exact), ->
+// bf16 (exact: at most five significant bits), in place: lane l of wave w
+// converts part p = 2w + (l >> 5) of token l & 31, whose code chunk sits in
+// column 4p + 3 (half 0) or 4p (half 1) and is read before any write.  The
+// scale word of a token holds the e4m3 scales of groups 4w..4w+3.
+__device__ __forceinline__ void fp4_convert(unsigned char* dst, const float* scales, int w, int l) {
+    const int t = l & 31, half = l >> 5, p = 2 * w + half;
+    const i32x4 raw = *(const i32x4*)(dst + lds_chunk(t, half ? 4 * p : 4 * p + 3) * 16);
+    const int sw = (int)(__float_as_uint(scales[t]) >> (16 * half));
+    const auto sc = __builtin_amdgcn_cvt_pk_f32_fp8(sw, false);      // scales of values 0..15, 16..31
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {                                     // output chunk h: values 8h..8h+7
+        const float s = sc[h >> 1];
+        const auto f0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(raw[h], 1.0f, 0);
+        const auto f1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(raw[h], 1.0f, 1);
+        const auto f2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(raw[h], 1.0f, 2);
+        const auto f3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(raw[h], 1.0f, 3);
+        float v[8] = {f0[0] * s, f0[1] * s, f1[0] * s, f1[1] * s, f2[0] * s, f2[1] * s, f3[0] * s, f3[1] * s};
+        *(bf16x8*)(dst + lds_chunk(t, 4 * p + h) * 16) = pack8(v);
+    }
+}
+
 // e4m3fn -> fp32 (exact), x scale in fp32, -> bf16 (round to nearest even), in
 // place: lane l of wave w converts part 2w + (l >> 5) of token l & 31.  The
 // scale word of a token holds one float32 (656-byte record: dims 128s..) or,
@@ -310,11 +338,12 @@ struct FillCtx {
 // 528-byte FP8 records of the 512-wide head (K = V = all 512 dims, no RoPE part)
 template <bool SPARSE, int KVF>
 __global__ void __launch_bounds__(kThreads, 1) decode_kernel(const DecodeArgs a) {
-    constexpr bool FP8 = KVF != 0;
-    constexpr bool D512 = KVF == 2;
+    constexpr bool FP8 = KVF != 0;                            // quantised cache (copied raw, dequantised in LDS)
+    constexpr bool FP4 = KVF == 3;
+    constexpr bool D512 = KVF >= 2;                           // 512-wide head, K = V
     constexpr int kQRow = D512 ? 1024 : kRowBytes;            // q row bytes
-    constexpr int kRec = D512 ? 528 : kFp8RowBytes;           // FP8 record bytes
-    static_assert(!D512 || SPARSE, "the 528-byte records are read through top-k indices");
+    constexpr int kRec = FP4 ? 288 : D512 ? 528 : kFp8RowBytes;   // record bytes
+    static_assert(!D512 || SPARSE, "the 528- and 288-byte records are read through top-k indices");
     __shared__ Smem sm;
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -479,19 +508,19 @@ __global__ void __launch_bounds__(kThreads, 1) decode_kernel(const DecodeArgs a)
             const int l = lane_id();
             const int dst = (int)(size_t)(lds_void_t*)&sm.tile[0][0] + opaque_tile_offset(it % kNBuf);
             const int sdst = (int)(size_t)(lds_void_t*)&sm.f8scale[wave][0];
-            const int tc = fp8_code_token(l), tr = fp8_rope_token(l, wave);
+            const int tc = FP4 ? fp4_code_token(l) : fp8_code_token(l), tr = fp8_rope_token(l, wave);
             const int wr = wave & 3;                       // waves w and w+4 copy the same RoPE columns
-            const int code_off = 64 * wave + 16 * (l >> 5);
+            const int code_off = FP4 ? 16 * (2 * wave + (l >> 5)) : 64 * wave + 16 * (l >> 5);
             const int rope_off = 528 + 16 * (2 * wr + (l >> 5));
-            const int scale_off = 512 + 4 * (wave >> 1);
-            const int code_lds = dst + (8 * wave + 2) * 512, rope_lds = dst + (64 + 2 * wr) * 512;
+            const int scale_off = FP4 ? 256 + 4 * wave : 512 + 4 * (wave >> 1);
+            const int code_lds = dst + (8 * wave + (FP4 ? 3 : 2)) * 512, rope_lds = dst + (64 + 2 * wr) * 512;
             if (SPARSE) {
                 const bool live = it < ns;
                 const int rc = live ? sm.rows[it & 3][tc] : -1;
                 const int rr_ = live ? sm.rows[it & 3][tr] : -1;
                 const int rs_ = (live && l < kSubTok) ? sm.rows[it & 3][l] : -1;
                 dma_global_x4<0>(fp8_row_addr(kv, rc, code_off, kRec), code_lds);
-                dma_global_x4<0>(fp8_row_addr(kv, rc, code_off + 32, kRec), code_lds + 2048);
+                if (!FP4) dma_global_x4<0>(fp8_row_addr(kv, rc, code_off + 32, kRec), code_lds + 2048);
                 if (!D512) dma_global_x4<0>(fp8_row_addr(kv, rr_, rope_off, kRec), rope_lds);
                 dma_global_x1(fp8_row_addr(kv, rs_, scale_off, kRec), sdst);
             } else {
@@ -507,7 +536,8 @@ __global__ void __launch_bounds__(kThreads, 1) decode_kernel(const DecodeArgs a)
             }
         };
         auto fp8_dequant = [&](int it) __attribute__((always_inline)) {
-            fp8_convert<D512>(sm.tile[0] + opaque_tile_offset(it % kNBuf), sm.f8scale[wave], wave, lane_id());
+            if constexpr (FP4) fp4_convert(sm.tile[0] + opaque_tile_offset(it % kNBuf), sm.f8scale[wave], wave, lane_id());
+            else fp8_convert<D512>(sm.tile[0] + opaque_tile_offset(it % kNBuf), sm.f8scale[wave], wave, lane_id());
         };
         // tile 0 lands before step 0
         if (FP8) {
@@ -861,7 +891,8 @@ __global__ void __launch_bounds__(kThreads, 1) decode_kernel(const DecodeArgs a)
 hipError_t launch_decode(const DecodeArgs& a, bool sparse, int kvf, hipStream_t stream) {
     const dim3 grid(a.num_parts * a.n_hblk), block(kThreads);
     if (sparse) {
-        if (kvf == 2) hipLaunchKernelGGL((decode_kernel<true, 2>), grid, block, 0, stream, a);
+        if (kvf == 3) hipLaunchKernelGGL((decode_kernel<true, 3>), grid, block, 0, stream, a);
+        else if (kvf == 2) hipLaunchKernelGGL((decode_kernel<true, 2>), grid, block, 0, stream, a);
         else if (kvf == 1) hipLaunchKernelGGL((decode_kernel<true, 1>), grid, block, 0, stream, a);
         else hipLaunchKernelGGL((decode_kernel<true, 0>), grid, block, 0, stream, a);
     } else {

@@ -54,7 +54,8 @@ struct GatherArgs {
     int batch, s_q, max_blocks, topk, causal, row_stride;
 };
 
-// kvf: 0 = bf16 rows of 576, 1 = 656-byte FP8 records, 2 = 528-byte FP8 records (512-wide head, sparse only)
+// kvf: 0 = bf16 rows of 576, 1 = 656-byte FP8 records, 2 = 528-byte FP8 records, 3 = 288-byte FP4 records
+// (2 and 3: 512-wide head, sparse only)
 hipError_t launch_decode(const DecodeArgs& a, bool sparse, int kvf, hipStream_t stream);
 hipError_t launch_metadata(const MetaArgs& a, hipStream_t stream);
 hipError_t launch_combine(const CombineArgs& a, hipStream_t stream);

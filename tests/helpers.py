@@ -25,7 +25,7 @@ def bits16(t):
 def kv_host(w):
     if w.kv_format == 'bf16':
         return bits16(w.kv).reshape(-1, 576)
-    return w.kv.detach().contiguous().cpu().numpy().reshape(-1, 656)
+    return w.kv.detach().contiguous().cpu().numpy().reshape(-1, int(w.kv.shape[-1]))
 
 
 def kv_host_rows(w, items):
@@ -36,7 +36,7 @@ def kv_host_rows(w, items):
     nrows = rows_dev.shape[0]
     idx = w.indices.cpu().numpy()
     need = np.unique(np.concatenate([idx[b, i][(idx[b, i] >= 0) & (idx[b, i] < nrows)] for b, i in items]))
-    raw = w.kv_format.startswith('fp8')        # byte records; bf16 rows otherwise
+    raw = w.kv_format != 'bf16'                # byte records; bf16 rows otherwise
     host = np.zeros((nrows, rows_dev.shape[1]), dtype=np.uint8 if raw else np.uint16)
     sel = torch.from_numpy(need.astype(np.int64)).to(w.kv.device)
     got = rows_dev[sel].cpu()

@@ -146,13 +146,14 @@ def test_prefill_rejects_bad_arguments_before_launch(lib):
     assert call(p3, 1000) == 1             # dense problem
 
 
-def test_528_byte_records_need_the_512_wide_head_and_top_k():
+@pytest.mark.parametrize("fmt", ["fp8_528", "fp4_288"])
+def test_512_wide_records_need_the_512_wide_head_and_top_k(fmt):
     import mla_decode_amd as mla
-    p = mla.make_problem(4, 2, 128, 64, topk=2048, kv_format="fp8_528")
+    p = mla.make_problem(4, 2, 128, 64, topk=2048, kv_format=fmt)
     assert p.d_qk == 512
     assert mla.plan(p, num_cus=256).num_partitions == 256
     with pytest.raises(mla.MlaError) as e:                       # dense paged decode is not offered
-        mla.plan(mla.make_problem(4, 1, 128, 64, 16, kv_format="fp8_528"), num_cus=256)
+        mla.plan(mla.make_problem(4, 1, 128, 64, 16, kv_format=fmt), num_cus=256)
     assert e.value.status == 2
     p.d_qk = 576                                                  # wrong head width for the format
     with pytest.raises(mla.MlaError) as e:
