@@ -80,7 +80,7 @@ def cpu_baseline_sparse(w):
         for i in range(w.s_q):
             rows = idx[b, i][(idx[b, i] >= 0) & (idx[b, i] < nrows)]
             got = kv_rows[torch.from_numpy(rows.astype(np.int64)).to(w.kv.device)].cpu()   # gathered on the GPU
-            kv = got.numpy() if w.kv_format.startswith("fp8") else got.view(torch.int16).numpy().view(np.uint16)
+            kv = got.numpy() if w.kv_format != "bf16" else got.view(torch.int16).numpy().view(np.uint16)
             t0 = time.perf_counter()
             A.decode_partial(q, kv, w.softmax_scale, np.arange(len(rows)), b, i, kv_format=w.kv_format)
             dt += time.perf_counter() - t0
@@ -208,7 +208,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--workload", default="dense_b64_s4096",
                     choices=["dense_b64_s4096", "fp8_sparse_topk2048", "fp8_sparse_topk32768", "sparse_prefill",
-                             "v41_sparse_topk2048"],
+                             "v41_sparse_topk2048", "fp4_sparse_topk2048"],
                     help="dense_b64_s4096 is the headline line; the others time the pages' FP8 sparse shape")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a 1 GiB device copy 5 times (reference for HBM byte counters)")
@@ -230,7 +230,7 @@ def main():
 
     import torch
     import mla_decode_amd as mla
-    from workloads import make_config, make_fp8_sparse, make_v41_sparse, flops_and_bytes
+    from workloads import make_config, make_fp8_sparse, make_v41_sparse, make_fp4_sparse, flops_and_bytes
 
     if args.workload == "sparse_prefill":
         return bench_prefill(args)
@@ -243,6 +243,9 @@ def main():
     elif args.workload.startswith("v41"):
         w = make_v41_sparse(128, 2, 128, pool_tokens_per_seq=32768, topk=2048, seed=4000, device=dev,
                             name="v41_sparse_b128_s2_topk2048")
+    elif args.workload.startswith("fp4"):
+        w = make_fp4_sparse(128, 2, 128, pool_tokens_per_seq=32768, topk=2048, seed=4100, device=dev,
+                            name="fp4_sparse_b128_s2_topk2048")
     else:
         w = make_fp8_sparse(int(args.workload.split("topk")[1]), device=dev)
     acct = flops_and_bytes(w)
@@ -342,18 +345,21 @@ def main():
     }
     if not headline:
         topk = w.topk
-        v41 = w.kv_format == "fp8_528"
-        rec = "528-byte records of the 512-wide head (e8m0 scales per 32 values)" if v41 else "656-byte records"
-        line["metric"] = (f"MLA sparse FP8 decode TFLOPS, µs/step at b=128,s_q=2,h_q=128,topk={topk}"
-                          f"{',528B records,d_qk=512' if v41 else ''} (1 GPU)")
-        line["config"] = {"workload": f"FP8 sparse absorbed-MLA decode b=128 s_q=2 h_q=128 top-k {topk} "
+        v41 = w.kv_format in ("fp8_528", "fp4_288")
+        rec = {"fp8_528": "528-byte records of the 512-wide head (e8m0 scales per 32 values)",
+               "fp4_288": "288-byte FP4 records of the 512-wide head (e2m1 pairs, e4m3 scales per 16 values)"}.get(
+                   w.kv_format, "656-byte records")
+        tag = {"fp8_528": ",528B records,d_qk=512", "fp4_288": ",288B FP4 records,d_qk=512"}.get(w.kv_format, "")
+        kind = "FP4" if w.kv_format == "fp4_288" else "FP8"
+        line["metric"] = f"MLA sparse {kind} decode TFLOPS, µs/step at b=128,s_q=2,h_q=128,topk={topk}{tag} (1 GPU)"
+        line["config"] = {"workload": f"{kind} sparse absorbed-MLA decode b=128 s_q=2 h_q=128 top-k {topk} "
                                       f"({rec}, {max(32768, 2 * topk)} cached tokens per request, "
                                       "every slot valid, N(0,1) sources)",
                           "batch": w.batch, "s_q": w.s_q, "h_q": w.h_q, "topk": topk,
                           "d_qk": 512 if v41 else 576, "d_v": 512,
-                          "block_size": 64, "kv_format": "fp8_528" if v41 else "fp8_656",
+                          "block_size": 64, "kv_format": w.kv_format if v41 else "fp8_656",
                           "step": "metadata + sparse decode (partial + combine)"}
-        line["roofline"] = {"bound": "mfma", "kernel": "decode_kernel<sparse, fp8 cache> (partial attention)",
+        line["roofline"] = {"bound": "mfma", "kernel": f"decode_kernel<sparse, {kind.lower()} cache> (partial attention)",
                             "achieved": round(kern_tflops, 1), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                             "frac": round(kern_tflops / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
                             "algorithmic_flops": flops, "us_per_launch": round(ms_kernel * 1e3, 2)}
