@@ -80,9 +80,11 @@ typedef enum { MLA_OUT_BF16 = 0, MLA_OUT_FP32 = 1 } mla_out_dtype_t;
 /* Problem shape.  Supported: h_kv = 1, d_qk = 576 (512 for MLA_KV_FP8_528 and MLA_KV_FP4_288), d_v = 512, block_size = 64
  * (FlashMLA README: the key cache has one head; d_v can only be 512).  Tensor
  * layouts:
- *   q            [batch, s_q, h_q, 576]              bfloat16
+ *   q            [batch, s_q, h_q, 576]              bfloat16 ([.., 512] for the 512-wide head)
  *   kv_cache     [num_blocks, 64, 1, 576] bfloat16   or
- *                [num_blocks, 64, 1, 656] uint8 (MLA_KV_FP8_656)
+ *                [num_blocks, 64, 1, 656] uint8 (MLA_KV_FP8_656) or
+ *                [num_blocks, 64, 1, 528] uint8 (MLA_KV_FP8_528) or
+ *                [num_blocks, 64, 1, 288] uint8 (MLA_KV_FP4_288)
  *   block_table  [batch, max_blocks_per_seq]         int32 page ids
  *   cache_seqlens[batch]                             int32, in [0, 64*max_blocks_per_seq]
  *   indices      [batch, s_q, topk]                  int32 page*64 + offset; -1 invalid
@@ -196,14 +198,15 @@ mla_status_t mla_sparse_decode_fwd(const mla_problem_t *problem, const void *q, 
  * every query row s of q [s_q, h_q, 576] attends to the rows
  * indices[s, 0, :] (device int32 [s_q, 1, topk]; entries < 0 or >= s_kv are
  * invalid) of a flat, unpaged cache kv [s_kv, 1, 576] bfloat16 (or
- * [s_kv, 1, 656] FP8 records), writing out [s_q, h_q, 512] and lse
+ * [s_kv, 1, 656 | 528 | 288] uint8 records, problem->kv_format telling which;
+ * q is [s_q, h_q, 512] with the 528- and 288-byte records), writing out [s_q, h_q, 512] and lse
  * [h_q, s_q].  It is the sparse decode of one request with s_q query tokens:
  * ``problem`` has batch = 1, s_q = the number of query rows (at most 16384
  * per call), topk > 0, causal 0 and num_blocks >= ceil(s_kv / 64); plan and
  * metadata are made as for mla_sparse_decode_fwd; topk_length ([s_q]) and
  * attn_sink ([h_q]) are optional.  The README copy gives this call on the
  * 512-wide head of its newer model; here it serves the 576-wide latent head
- * of the decode path.  Errors: as mla_sparse_decode_fwd, plus INVALID_ARG
+ * of the decode path as well as that 512-wide head.  Errors: as mla_sparse_decode_fwd, plus INVALID_ARG
  * when batch != 1 or s_kv is not in [1, num_blocks*64]. */
 mla_status_t mla_sparse_prefill_fwd(const mla_problem_t *problem, int32_t s_kv, const void *q, const void *kv,
                                     const int32_t *indices, const int32_t *topk_length, const float *attn_sink,
