@@ -97,6 +97,21 @@ FP8_MUTANTS = [
      "rope_bits = np.ascontiguousarray(flat[:, SCALE_OFFSET:SCALE_OFFSET + 2 * ROPE])"),
     ("scale applied after rounding", "prod = (vals * tile_scale).astype(np.float32)",
      "prod = (f32_to_bf16_bits_rne(vals).astype(np.float32) * 0 + vals * tile_scale * 1.0001).astype(np.float32)"),
+    # 528-byte records
+    ("e8m0 bias 128", "out = np.ldexp(1.0, e - 127)", "out = np.ldexp(1.0, e - 128)"),
+    ("528-byte scales in reverse order", "out = vals * np.repeat(scales, V41_GROUP, axis=1)",
+     "out = vals * np.repeat(scales[:, ::-1], V41_GROUP, axis=1)"),
+    # 288-byte FP4 records
+    ("FP4 nibbles swapped", "codes[:, 0::2] = packed & 0xF          # even index: low nibble\n    codes[:, 1::2] = packed >> 4",
+     "codes[:, 0::2] = packed >> 4\n    codes[:, 1::2] = packed & 0xF"),
+    ("FP4 scale group of 32 values", "out = e2m1_decode(codes) * np.repeat(scales, FP4_GROUP, axis=1)",
+     "out = e2m1_decode(codes) * np.repeat(scales[:, :16], 2 * FP4_GROUP, axis=1)"),
+    ("FP4 scales read from the code bytes", "scales = e4m3fn_decode(flat[:, FP4_DIM // 2:])",
+     "scales = e4m3fn_decode(flat[:, :FP4_DIM // 16])"),
+    ("e2m1 exponent bias 0", "np.ldexp(1.0 + 0.5 * m, (e - 1).astype(np.int32))",
+     "np.ldexp(1.0 + 0.5 * m, e.astype(np.int32))"),
+    ("e2m1 subnormal read as normal", "mag = np.where(e == 0, 0.5 * m,", "mag = np.where(e == 0, 1.0 * m,"),
+    ("e2m1 sign from bit 2", "sign = np.where(c & 8, -1.0, 1.0)", "sign = np.where(c & 4, -1.0, 1.0)"),
 ]
 
 
