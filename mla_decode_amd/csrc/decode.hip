@@ -828,7 +828,10 @@ __global__ void __launch_bounds__(kThreads, 1) decode_kernel(const DecodeArgs a)
         const bool final_out = (nsplit == 1);
         const int b = j / a.s_q, iq = j - b * a.s_q;
         if (final_out || (slot >= 0 && slot < a.max_slots)) {
-            const float lse_v = l_run > 0.f ? (c * m_run + log2f(l_run)) * 0.69314718055994531f : -INFINITY;
+            // l = 0: nothing visible (lse -inf, weight 0 in the merge); l NaN (a NaN
+            // in q or the cache): lse NaN, so the merge propagates it
+            const float lse_v = l_run > 0.f ? (c * m_run + log2f(l_run)) * 0.69314718055994531f
+                                             : (l_run == 0.f ? -INFINITY : __builtin_nanf(""));
             float inv = l_run > 0.f ? 1.f / l_run : 0.f;
             // attention sink: a final output is scaled by exp(lse) / (exp(lse) + exp(sink))
             if (final_out && a.attn_sink && head_ok) inv *= 1.f / (1.f + __expf(a.attn_sink[head] - lse_v));
