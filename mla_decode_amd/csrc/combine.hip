@@ -25,6 +25,7 @@ __global__ void __launch_bounds__(256) combine_kernel(const CombineArgs a) {
     constexpr int kSplitChunk = 4;
     float m = -INFINITY, wsum = 0.f;
     float o[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    bool nan_lse = false;   // a split whose softmax sum was NaN (a NaN in q or the cache) makes the row NaN
     for (int k0 = s0; k0 < s1; k0 += kSplitChunk) {
         float lk[kSplitChunk];
         f32x4 u[kSplitChunk], v[kSplitChunk];
@@ -54,7 +55,10 @@ __global__ void __launch_bounds__(256) combine_kernel(const CombineArgs a) {
         }
         float mc = m;
 #pragma unroll
-        for (int c = 0; c < kSplitChunk; ++c) mc = fmaxf(mc, lk[c]);
+        for (int c = 0; c < kSplitChunk; ++c) {
+            mc = fmaxf(mc, lk[c]);
+            nan_lse |= lk[c] != lk[c];
+        }
         if (mc == -INFINITY) continue;                       // nothing finite yet
         const float sc = m == -INFINITY ? 0.f : __expf(m - mc);
         wsum *= sc;
@@ -84,6 +88,11 @@ __global__ void __launch_bounds__(256) combine_kernel(const CombineArgs a) {
     } else {
 #pragma unroll
         for (int e = 0; e < 8; ++e) o[e] = 0.f;
+    }
+    if (nan_lse) {
+        lse_v = __builtin_nanf("");
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o[e] = lse_v;
     }
     const int64_t off = ((int64_t)item * H + h) * kDv + lane * 8;
     if (a.out_fp32) {

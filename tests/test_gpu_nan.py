@@ -54,3 +54,20 @@ def test_fp4_nan_scale():
     kv = w.kv.cpu().numpy().reshape(-1, 288)
     for num_cus in (0, 7):
         print(num_cus, _check(w, [(2, 0)], num_cus, kv=kv), flush=True)
+
+
+def test_nan_in_one_head_of_q():
+    """Every partition of the item sees the NaN (it is in q), so all its
+    splits report a NaN lse; only that head of that query token is NaN."""
+    print("q nan", flush=True)
+    w = make_dense(3, 1, 128, [3000, 1500, 900], seed=73, device=DEV)
+    w.q[1, 0, 5, 7] = float("nan")
+    ro0, rl0 = oracle(w)
+    for num_cus in (0, 3):
+        go, gl, _ = run_library(w, num_cus=num_cus)
+        ro, rl = ro0.copy(), rl0.copy()
+        assert np.isnan(ro[1, 0, 5]).all() and np.isnan(rl[1, 5, 0])
+        assert np.isnan(go[1, 0, 5]).all() and np.isnan(gl[1, 5, 0]), num_cus
+        go[1, 0, 5] = ro[1, 0, 5] = 0.0
+        gl[1, 5, 0] = rl[1, 5, 0] = 0.0
+        print(num_cus, compare(go, gl, ro, rl), flush=True)
