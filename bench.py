@@ -209,7 +209,9 @@ def main():
     ap.add_argument("--workload", default="dense_b64_s4096",
                     choices=["dense_b64_s4096", "fp8_sparse_topk2048", "fp8_sparse_topk32768", "sparse_prefill",
                              "v41_sparse_topk2048", "fp4_sparse_topk2048"],
-                    help="dense_b64_s4096 is the headline line; the others time the pages' FP8 sparse shape")
+                    help="dense_b64_s4096 is the headline line; the others time the pages' sparse decode shape "
+                         "(b=128, s_q=2, top-k 2048 or 32768) over the 656-, 528- and 288-byte record caches, "
+                         "and top-k sparse prefill")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a 1 GiB device copy 5 times (reference for HBM byte counters)")
     args = ap.parse_args()
