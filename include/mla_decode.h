@@ -48,7 +48,7 @@
 extern "C" {
 #endif
 
-#define MLA_DECODE_ABI_VERSION 2
+#define MLA_DECODE_ABI_VERSION 3
 
 typedef enum {
     MLA_OK = 0,
@@ -128,7 +128,7 @@ typedef struct {
 typedef struct {
     mla_problem_t sig;           /* problem the plan was made for */
     int32_t num_partitions;      /* P: workgroup columns of the split-KV grid */
-    int32_t num_head_blocks;     /* ceil(h_q / 128) */
+    int32_t num_head_blocks;     /* ceil(h_q / 64) for dense decode over a bf16 cache, else ceil(h_q / 128) */
     int32_t fixed_overhead;      /* F: per-item cost added by the scheduler */
     int32_t max_splits;          /* upper bound of split slots: batch*s_q + P */
     void *dev;                   /* caller-owned device buffer, >= bytes */
@@ -222,25 +222,30 @@ mla_status_t mla_sparse_prefill_fwd(const mla_problem_t *problem, int32_t s_kv, 
  * and receives out[b, i, :, :] and lse[b, :, i].  An item with no slot, or
  * whose partials are all -inf, gets out = 0 and lse = -inf.  attn_sink
  * ([h_q] float32 or NULL) scales each merged row as at the top of this file.
- * All pointers are device memory.  Errors: INVALID_ARG, HIP. */
+ * All pointers are device memory.  Errors: INVALID_ARG, UNSUPPORTED when
+ * num_items * h_q is 2^29 or more, HIP. */
 mla_status_t mla_combine(int32_t num_items, int32_t h_q, int32_t s_q, const float *o_part,
                          const float *lse_part, const int32_t *split_offsets, const float *attn_sink,
                          int32_t out_dtype, void *out, float *lse, void *stream);
 
-/* Test hook: the partial-attention kernel of mla_decode_fwd /
+/* Test and measurement hook: the partial-attention kernel of mla_decode_fwd /
  * mla_sparse_decode_fwd alone, without the LSE combine.  Items whose KV range
  * lies in one partition get out and lse as usual; every other item leaves its
- * normalised partials in ``workspace`` (layout as in mla_combine: o_part
- * first, then lse_part at float offset max_splits*h_q*512) and its out/lse
- * untouched.  ``table_or_indices`` is block_table (dense) or indices (sparse);
- * cache_seqlens is ignored for sparse problems, topk_length for dense ones;
- * attn_sink applies to the outputs this call writes.  Same errors as
- * mla_decode_fwd. */
+ * normalised partials in ``workspace`` and its out/lse untouched.
+ * partial_format 0: float32 partials in the layout mla_combine takes (o_part
+ * first, then lse_part at float offset max_splits*h_q*512).  partial_format 1:
+ * the format mla_decode_fwd itself writes before its combine (float16 scaled
+ * per lane by a power of two when the output is bf16, float32 otherwise), so
+ * that the launch is the one a decode step makes.  ``table_or_indices`` is
+ * block_table (dense) or indices (sparse); cache_seqlens is ignored for sparse
+ * problems, topk_length for dense ones; attn_sink applies to the outputs this
+ * call writes.  Same errors as mla_decode_fwd, plus INVALID_ARG for another
+ * partial_format. */
 mla_status_t mla_debug_decode_partial(const mla_problem_t *problem, const void *q, const void *kv_cache,
                                       const int32_t *table_or_indices, const int32_t *cache_seqlens,
                                       const int32_t *topk_length, const float *attn_sink,
                                       const mla_metadata_t *meta, void *workspace, size_t workspace_bytes,
-                                      void *out, float *lse, void *stream);
+                                      void *out, float *lse, int32_t partial_format, void *stream);
 
 /* Test hook for the row resolution: writes, for every item j and KV slot t < tiles_j*64, the
  * physical cache row the decode kernels read for that slot, or -1 where the

@@ -210,8 +210,9 @@ def debug_gather_rows(problem, table_or_indices, cache_seqlens, rows_out, stream
 
 
 def debug_decode_partial(problem, q, kv_cache, table_or_indices, cache_seqlens, meta, workspace, out, lse,
-                         stream=None, topk_length=None, attn_sink=None):
-    """Test hook: the partial-attention kernel alone (mla_debug_decode_partial)."""
+                         stream=None, topk_length=None, attn_sink=None, production=False):
+    """Test hook: the partial-attention kernel alone (mla_debug_decode_partial).  ``production``: split
+    partials in the decode call's own format (the launch a decode step makes) instead of mla_combine's."""
     lib = _lib.load()
     _need(q, "q", torch.bfloat16)
     _need(kv_cache, "kv_cache", None)
@@ -223,7 +224,7 @@ def debug_decode_partial(problem, q, kv_cache, table_or_indices, cache_seqlens, 
     _lib.check("mla_debug_decode_partial", lib.mla_debug_decode_partial(
         ctypes.byref(problem), _ptr(q), _ptr(kv_cache), _ptr(table_or_indices), _ptr(cache_seqlens), _ptr(tl),
         _ptr(sink), ctypes.byref(meta), _ptr(workspace), workspace.numel() * workspace.element_size(), _ptr(out), _ptr(lse),
-        _stream(stream)))
+        1 if production else 0, _stream(stream)))
 
 
 class Decoder:
@@ -246,11 +247,12 @@ class Decoder:
         get_decode_metadata(self.problem, cache_seqlens, self.meta, self.meta_buf, stream, topk_length)
 
     def decode_partial(self, q, kv_cache, block_table=None, cache_seqlens=None, indices=None, stream=None,
-                       topk_length=None, attn_sink=None):
-        """The partial-attention kernel alone (test and measurement hook)."""
+                       topk_length=None, attn_sink=None, production=False):
+        """The partial-attention kernel alone (test and measurement hook); ``production`` keeps the decode
+        call's own partial format."""
         toi = indices if self.problem.topk > 0 else block_table
         debug_decode_partial(self.problem, q, kv_cache, toi, cache_seqlens, self.meta, self.workspace, self.out,
-                             self.lse, stream, topk_length, attn_sink)
+                             self.lse, stream, topk_length, attn_sink, production)
 
     def decode(self, q, kv_cache, block_table=None, cache_seqlens=None, indices=None, stream=None,
                topk_length=None, attn_sink=None):

@@ -10,7 +10,7 @@ import os
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libmla_decode.so")
 
-ABI_VERSION = 2   # MLA_DECODE_ABI_VERSION of the header this binding mirrors
+ABI_VERSION = 3   # MLA_DECODE_ABI_VERSION of the header this binding mirrors
 MLA_OK = 0
 STATUS_NAMES = {0: "MLA_OK", 1: "MLA_ERR_INVALID_ARG", 2: "MLA_ERR_UNSUPPORTED", 3: "MLA_ERR_WORKSPACE_TOO_SMALL",
                 4: "MLA_ERR_METADATA_MISMATCH", 5: "MLA_ERR_HIP"}
@@ -87,7 +87,7 @@ def load():
     lib.mla_debug_gather_rows.argtypes = [P(Problem), vp, vp, vp, vp, vp]
     lib.mla_debug_decode_partial.restype = ctypes.c_int
     lib.mla_debug_decode_partial.argtypes = [P(Problem), vp, vp, vp, vp, vp, vp, P(Metadata), vp, ctypes.c_size_t,
-                                             vp, vp, vp]
+                                             vp, vp, i32, vp]
     _lib = lib
     return lib
 

@@ -36,6 +36,11 @@ mla_status_t device_cus(int32_t* out) {
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
+// Dense decode over a bf16 cache runs the 64-heads-per-workgroup kernel; the
+// other formats and the sparse calls run the 128-heads-per-workgroup one.
+bool uses_decode64(const mla_problem_t* p) { return p->topk == 0 && p->kv_format == MLA_KV_BF16_576; }
+int32_t heads_per_block(const mla_problem_t* p) { return uses_decode64(p) ? 64 : mla::kHeadsPerWG; }
+
 mla_status_t validate(const mla_problem_t* p) {
     if (!p) return MLA_ERR_INVALID_ARG;
     if (p->batch < 1 || p->s_q < 1 || p->h_q < 1 || p->num_blocks < 1) return MLA_ERR_INVALID_ARG;
@@ -79,7 +84,7 @@ mla_status_t check_meta(const mla_problem_t* p, const mla_metadata_t* m) {
     if (!m || !m->dev || !aligned16(m->dev)) return MLA_ERR_INVALID_ARG;
     if (!same_problem(m->sig, *p)) return MLA_ERR_METADATA_MISMATCH;
     const int64_t items = (int64_t)p->batch * p->s_q;
-    if (m->num_partitions < 1 || m->num_head_blocks != (p->h_q + mla::kHeadsPerWG - 1) / mla::kHeadsPerWG ||
+    if (m->num_partitions < 1 || m->num_head_blocks != (p->h_q + heads_per_block(p) - 1) / heads_per_block(p) ||
         m->fixed_overhead != kFixedOverhead || m->max_splits != items + m->num_partitions ||
         m->bytes < meta_bytes(m->num_partitions, items))
         return MLA_ERR_METADATA_MISMATCH;
@@ -103,7 +108,7 @@ mla_status_t run_decode(const mla_problem_t* p, bool sparse, const void* q, cons
                         const int32_t* block_table, const int32_t* cache_seqlens, const int32_t* indices,
                         const int32_t* topk_length, const float* attn_sink, const mla_metadata_t* meta,
                         void* ws, size_t ws_bytes, void* out, float* lse, void* stream, bool run_combine = true,
-                        int64_t num_rows = 0) {
+                        int64_t num_rows = 0, bool production_partials = true) {
     mla_status_t st = validate(p);
     if (st != MLA_OK) return st;
     if (sparse != (p->topk > 0)) return MLA_ERR_INVALID_ARG;
@@ -130,10 +135,10 @@ mla_status_t run_decode(const mla_problem_t* p, bool sparse, const void* q, cons
     a.lse_part = (float*)ws + slots * p->h_q * mla::kDv;
     // With a bf16 output the split partials travel as scaled float16 (half the
     // bytes of the partial write and of the combine's read), their scales in
-    // the second half of the float32 partial area; the test hook without the
-    // combine keeps float32 partials.
-    a.part_fp16 = run_combine && p->out_dtype != MLA_OUT_FP32;
-    a.o_exp = (uint32_t*)((char*)ws + slots * p->h_q * mla::kDv * 2);
+    // the second half of the float32 partial area; the test hook keeps float32
+    // partials unless it is asked for the decode call's own format.
+    a.part_fp16 = production_partials && p->out_dtype != MLA_OUT_FP32;
+    a.o_exp8 = (unsigned char*)ws + slots * p->h_q * mla::kDv * 2;
     a.out = out;
     a.lse = lse;
     a.num_rows = num_rows > 0 ? num_rows : (int64_t)p->num_blocks * kBlock;   // rows a valid index may name
@@ -150,12 +155,13 @@ mla_status_t run_decode(const mla_problem_t* p, bool sparse, const void* q, cons
     a.scale_log2 = p->softmax_scale * 1.4426950408889634f;
     a.rescale_tau = p->rescale_threshold;
     hipStream_t s = (hipStream_t)stream;
-    if (mla::launch_decode(a, sparse, p->kv_format, s) != hipSuccess) return MLA_ERR_HIP;
+    const hipError_t e = uses_decode64(p) ? mla::launch_decode64(a, s) : mla::launch_decode(a, sparse, p->kv_format, s);
+    if (e != hipSuccess) return MLA_ERR_HIP;
 
     mla::CombineArgs c{};
     c.o_part = a.o_part;
     c.lse_part = a.lse_part;
-    c.o_exp = a.o_exp;
+    c.o_exp8 = a.o_exp8;
     c.part_fp16 = a.part_fp16;
     c.split_offsets = a.meta + mla::kMetaHeader + mla::kMetaRec * meta->num_partitions;
     c.attn_sink = attn_sink;
@@ -197,7 +203,7 @@ mla_status_t mla_plan(const mla_problem_t* problem, int32_t num_cus, mla_metadat
         st = device_cus(&num_cus);
         if (st != MLA_OK) return st;
     }
-    const int32_t hblk = (problem->h_q + mla::kHeadsPerWG - 1) / mla::kHeadsPerWG;
+    const int32_t hblk = (problem->h_q + heads_per_block(problem) - 1) / heads_per_block(problem);
     int32_t parts = num_cus / hblk;
     if (parts < 1) parts = 1;
     const int64_t items = (int64_t)problem->batch * problem->s_q;
@@ -289,12 +295,12 @@ mla_status_t mla_debug_decode_partial(const mla_problem_t* problem, const void* 
                                       const int32_t* table_or_indices, const int32_t* cache_seqlens,
                                       const int32_t* topk_length, const float* attn_sink,
                                       const mla_metadata_t* meta, void* workspace, size_t workspace_bytes,
-                                      void* out, float* lse, void* stream) {
-    if (!problem) return MLA_ERR_INVALID_ARG;
+                                      void* out, float* lse, int32_t partial_format, void* stream) {
+    if (!problem || (partial_format != 0 && partial_format != 1)) return MLA_ERR_INVALID_ARG;
     const bool sparse = problem->topk > 0;
     return run_decode(problem, sparse, q, kv_cache, sparse ? nullptr : table_or_indices,
                       sparse ? nullptr : cache_seqlens, sparse ? table_or_indices : nullptr, topk_length,
-                      attn_sink, meta, workspace, workspace_bytes, out, lse, stream, false);
+                      attn_sink, meta, workspace, workspace_bytes, out, lse, stream, false, 0, partial_format == 1);
 }
 
 mla_status_t mla_debug_gather_rows(const mla_problem_t* problem, const int32_t* table_or_indices,

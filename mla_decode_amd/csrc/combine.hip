@@ -39,11 +39,11 @@ __global__ void __launch_bounds__(256) combine_kernel(const CombineArgs a) {
                 lk[c] = a.lse_part[(int64_t)k * H + h];
                 if (a.part_fp16) {
                     // float16 partial scaled by 2^-E; dims lane*8 + 0..3 use byte
-                    // 2 kh, dims + 4..7 byte 2 kh + 1 of the scale word (kh = lane / 32)
+                    // 2 q, dims + 4..7 byte 2 q + 1 of the head's exponents (q = lane / 16)
                     typedef __attribute__((__vector_size__(8 * sizeof(_Float16)))) _Float16 f16x8;
                     const f16x8 x = *(const f16x8*)((const _Float16*)a.o_part + ((int64_t)k * H + h) * kDv + lane * 8);
-                    const uint32_t ew = a.o_exp[(int64_t)k * H + h] >> (16 * (lane >> 5));
-                    const int e0 = (int)(signed char)(ew & 0xff), e1 = (int)(signed char)((ew >> 8) & 0xff);
+                    const unsigned char* ex = a.o_exp8 + ((int64_t)k * H + h) * 8 + 2 * (lane >> 4);
+                    const int e0 = (int)(signed char)ex[0], e1 = (int)(signed char)ex[1];
                     u[c] = f32x4{ldexpf((float)x[0], e0), ldexpf((float)x[1], e0), ldexpf((float)x[2], e0), ldexpf((float)x[3], e0)};
                     v[c] = f32x4{ldexpf((float)x[4], e1), ldexpf((float)x[5], e1), ldexpf((float)x[6], e1), ldexpf((float)x[7], e1)};
                 } else {

@@ -6,11 +6,12 @@
 // registers each; wave w owns head block hb = w >> 1 (32 heads) and half
 // kh = w & 1.  Each page is computed as two 32-token tiles:
 //
-//   fill   tiles are copied global -> LDS with 16-byte buffer loads that
-//          write LDS directly (bf16 cache; three LDS buffers: the tile being
-//          multiplied, the previous one for PV, the next one landing), or
-//          loaded to registers, dequantised and stored (FP8 cache).  Masked
-//          tokens fall outside the buffer range and land as zeros;
+//   fill   tiles are copied global -> LDS with 16-byte loads that write LDS
+//          directly (three LDS buffers: the tile being multiplied, the
+//          previous one for PV, the next one landing).  Quantised records
+//          (FP8, FP4) are copied raw and dequantised in place in LDS by the
+//          waves that copied them.  Masked tokens fall outside the buffer
+//          range (or read a zero row) and land as zeros;
 //   QK     the two waves of a head block split the 576 dims: wave kh runs
 //          S^T = K Q^T over latent dims 256*kh.. and half of the RoPE dims
 //          with v_mfma_f32_32x32x16_bf16 (Q in registers, RoPE part of Q in
@@ -30,7 +31,8 @@
 // SIMD work at the same time.
 //
 // Items whose KV range sits in one partition write out/lse directly; split
-// items write normalised fp32 partials for the combine kernel.
+// items write normalised partials for the combine kernel: float32 when the
+// output is float32, otherwise float16 scaled per lane by a power of two.
 
 #include "common.h"
 #include "kernels.h"
@@ -838,8 +840,8 @@ __global__ void __launch_bounds__(kThreads, 1) decode_kernel(const DecodeArgs a)
             // Split partials in float16 (when the output is bf16): each lane scales
             // its 128 values by 2^-E, E from the exponent of their largest
             // magnitude, so they lie in [-1, 1) and cannot overflow; E is stored
-            // as byte 2 kh + half of the head's scale word (the byte of every
-            // dim d with d / 256 = kh and d % 8 / 4 = half).
+            // in the head's exponent bytes 2 q + half of the dims d it holds
+            // (q = d / 128 in {2 kh, 2 kh + 1}, half = d % 8 / 4).
             const bool part16 = !final_out && a.part_fp16;
             int E = 0;
             if (part16 && head_ok) {
@@ -852,7 +854,9 @@ __global__ void __launch_bounds__(kThreads, 1) decode_kernel(const DecodeArgs a)
                 const int be = (int)((__float_as_uint(amax) >> 23) & 0xff);   // biased exponent
                 E = amax > 0.f ? (be == 0 ? -125 : be - 126) : 0;              // amax * 2^-E < 1
                 E = E > 127 ? 127 : E;
-                ((unsigned char*)a.o_exp)[((int64_t)slot * H + head) * 4 + 2 * kh + half] = (unsigned char)(signed char)E;
+                // the lane's dims span quarters 2 kh and 2 kh + 1 of the head
+                a.o_exp8[((int64_t)slot * H + head) * 8 + 4 * kh + half] = (unsigned char)(signed char)E;
+                a.o_exp8[((int64_t)slot * H + head) * 8 + 4 * kh + 2 + half] = (unsigned char)(signed char)E;
             }
             if (head_ok) {
 #pragma unroll

@@ -1,0 +1,608 @@
+// Split-KV partial-attention kernel for absorbed-MLA decode on gfx950, dense
+// bf16 cache: 64 query heads per workgroup, waves split by role.
+//
+// A workgroup computes 64 heads of one scheduler partition (a contiguous run
+// of 32-token KV tiles, possibly spanning several items).  The two workgroups
+// that hold the two head blocks of a partition are placed on the same XCD, so
+// the second read of every KV tile is served by that XCD's L2.  Halving the
+// heads per workgroup halves the fixed register state (the fp32 output
+// accumulator and Q), which is what lets every role below run without
+// spilling and with deep operand prefetch.
+//
+// Eight waves, two per SIMD (the dispatcher puts wave w on SIMD w % 4):
+//   QK waves (2, 3)     head block hb = w - 2 (32 heads).  Q for all 576 dims
+//                       lives in registers (144 VGPRs), so the full scores
+//                       S^T = K Q^T of a tile are one wave's MFMA chain (two
+//                       alternating accumulators) and need no exchange with
+//                       another wave.  While the MFMAs of tile k+1 run, the
+//                       same wave does the exact online softmax of tile k:
+//                       running max raised whenever the tile holds a larger
+//                       score, p = exp2(s c - m c), l sums the fp32 p, P is
+//                       rounded to bf16 and handed to the PV waves in LDS
+//                       with the rescale factor alpha.
+//   PV waves (0, 1, 4, 5)  output dims 128 q .. 128 q + 127 of all 64 heads
+//                       (q = 0, 1, 2, 3): acc O^T += V^T P^T, the V^T operand
+//                       read straight from the row-major tile with
+//                       ds_read_b64_tr_b16, each fragment feeding the MFMAs of
+//                       both head blocks.  Before a block of O takes its MFMAs
+//                       it is rescaled by alpha (skipped when no head's max
+//                       rose), so the multiplies of one block overlap the MFMAs
+//                       of the previous one.
+//   copy waves (6, 7)   stage tiles global -> LDS with 16-byte buffer loads
+//                       that write LDS directly (tokens past the valid count
+//                       fall outside the buffer range and land as zeros), and
+//                       publish each tile's valid token count.
+//
+// Step k (one workgroup barrier per step, LDS ring of four 32-token tiles):
+//   QK waves     softmax(k) and QK(k+1)        reads tile k+1
+//   PV waves     rescale and PV(k-1)           reads tile k-1
+//   copy waves   copy of tile k+2              writes the buffer of tile k-2
+// so every SIMD has MFMA and vector work from two waves at once.
+//
+// Items whose KV range sits in one partition write out/lse directly; split
+// items write normalised partials (float16 scaled per lane by a power of two
+// when the output is bf16, float32 otherwise) for the combine kernel.
+
+#include "common.h"
+#include "kernels.h"
+
+namespace mla {
+
+namespace {
+
+constexpr int kH = 64;                          // query heads per workgroup
+constexpr int kT = 512;                         // threads (8 waves)
+constexpr int kTileB = kSubTok * kRowBytes;     // 36864 bytes per 32-token tile
+constexpr int kRing = 4;                        // LDS tile buffers
+constexpr int kQkLA = 6;                        // K fragments in flight (QK waves)
+constexpr int kPvLA = 4;                        // V fragments in flight (PV waves)
+
+// Small arrays first: LDS instructions encode at most a 16-bit immediate
+// offset, so arrays addressed with constant offsets must sit below 64 KiB.
+struct __attribute__((aligned(16))) Smem64 {
+    bf16x8 p[2][2][2][64];          // P(k) as B fragments [k & 1][head block][k-step][lane]
+    float alpha[2][2][32];          // rescale factor of O for tile k [k & 1][head block][head]
+    float fin_inv[kH];              // epilogue: output scale 1/l (times the sink factor)
+    float fin_pad[kH];
+    int valid[kRing];               // valid tokens of the tile in each buffer
+    int pad[4];
+    unsigned char pf_sink[256];     // destination of the L2 prefetch loads (never read)
+    unsigned char tile[kRing][kTileB];   // 32-token tiles (bf16, swizzled columns, see lds_chunk)
+};
+
+// LDS layout of a 32-token tile (72 columns of 16 bytes per token): 36
+// blocks of 1 KiB, block 4 (c / 8) + t / 8 holding the 128-byte line c / 8 of
+// tokens 8 (t / 8) .. + 7; inside a block token t sits at chunk 8 (t % 8) +
+// ((c % 8) ^ swz(t)), swz(t) = (t % 8) ^ ((t / 8) % 2).  A copy instruction then
+// reads eight whole lines, and 16 consecutive tokens of one column fall on 16
+// distinct 16-byte bank groups (64 banks of 4 bytes).  Returns the chunk index
+// within the tile (for c < 64; RoPE columns 64..71 likewise).
+__device__ __forceinline__ int tile_chunk(int t, int c) {
+    const int swz = (t & 7) ^ ((t >> 3) & 1);
+    return 64 * (4 * (c >> 3) + (t >> 3)) + 8 * (t & 7) + ((c & 7) ^ swz);
+}
+
+__device__ __forceinline__ bf16x4 tr_read64(const unsigned char* p) {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((__attribute__((address_space(3))) bf16x4*)(p));
+}
+
+// Uniform byte offset of tile buffer ``idx``, hidden from the optimiser so
+// that it adds it to a few lane bases instead of keeping one set of lane
+// addresses per buffer.
+__device__ __forceinline__ int ring_offset(int idx) {
+    int off = idx * kTileB;
+    __asm__ volatile("" : "+s"(off));
+    return off;
+}
+
+__device__ __forceinline__ int lane_id64() {
+    unsigned m = ~0u;
+    __asm__ volatile("" : "+s"(m));
+    return (int)__builtin_amdgcn_mbcnt_hi(m, __builtin_amdgcn_mbcnt_lo(m, 0u));
+}
+
+__device__ __forceinline__ i32x4 rsrc(const void* base, int num_records) {
+    const uint64_t p = (uint64_t)base;
+    i32x4 r;
+    r[0] = (int)(uint32_t)p;
+    r[1] = (int)((uint32_t)(p >> 32) & 0xffffu);
+    r[2] = num_records;
+    r[3] = 0x00020000;
+    return r;
+}
+
+// 16-byte-per-lane global -> LDS copy (one wave instruction writes 1 KiB of
+// LDS at M0 + offset + 16 lane; the immediate offset moves the global source
+// as well, so M0 is the destination minus the immediate).  Issued through
+// inline assembly so that the compiler does not wait for it before unrelated
+// LDS reads; the issuing wave waits with vmcnt before the step barrier.
+template <int IMM>
+__device__ __forceinline__ void copy_x4(const i32x4& rs, int voff, int lds) {
+    __asm__ volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen offset:%3 lds"
+                     :: "s"(lds - IMM), "v"(voff), "s"(rs), "i"(IMM) : "memory", "m0");
+}
+
+// 4-byte-per-lane global -> LDS load into a 256-byte sink: brings the source
+// lines into L2 ahead of their copy; nothing reads the sink
+__device__ __forceinline__ void prefetch_x1(const i32x4& rs, int voff, int lds) {
+    __asm__ volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, 0 offen lds"
+                     :: "s"(lds), "v"(voff), "s"(rs) : "memory", "m0");
+}
+
+__device__ __forceinline__ void barrier_lds() {
+    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0); vmcnt, expcnt untouched
+    __asm__ volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    __asm__ volatile("" ::: "memory");
+}
+
+constexpr int kGrpMfma = 0x008, kGrpValu = 0x002, kGrpDsRead = 0x100, kGrpDsWrite = 0x200;
+
+template <int V>
+struct Int {
+    static constexpr int value = V;
+};
+template <int B, int E, class F>
+__device__ __forceinline__ void unroll(F&& f) {
+    if constexpr (B < E) {
+        f(Int<B>{});
+        unroll<B + 1, E>(f);
+    }
+}
+
+}  // namespace
+
+__global__ void __launch_bounds__(kT, 1) decode64_kernel(const DecodeArgs a) {
+    __shared__ Smem64 sm;
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    // roles
+    const bool is_qk = wave == 2 || wave == 3;
+    const bool is_copy = wave >= 6;
+    const int hbq = wave - 2;                                   // QK waves: head block
+    const int dq = (wave & 1) + 2 * (wave >> 2);                // PV waves 0, 1, 4, 5 -> dim quarter 0, 1, 2, 3
+    const int cw = wave - 6;                                    // copy waves: 0, 1
+
+    // workgroup -> (partition, head block): each XCD (blockIdx % 8) gets a
+    // contiguous run of linear indices, so the head blocks of a partition and
+    // neighbouring partitions share an L2.
+    int part, hblk;
+    {
+        const int G = a.num_parts * a.n_hblk;
+        const int x = blockIdx.x & 7, k = blockIdx.x >> 3;
+        const int q8 = G >> 3, r8 = G & 7;
+        const int lin = x * q8 + min(x, r8) + k;
+        part = lin / a.n_hblk;
+        hblk = lin - part * a.n_hblk;
+    }
+    const int32_t* rec = a.meta + kMetaHeader + kMetaRec * part;
+    const int32_t* so = a.meta + kMetaHeader + kMetaRec * a.num_parts;
+    const int jb = sload(rec + 0), tbeg = sload(rec + 1), je = sload(rec + 2), tend = sload(rec + 3);
+    const int slot0 = sload(rec + 4);
+    const int N = a.batch * a.s_q;
+    const int H = a.h_q;
+    const float c = a.scale_log2;
+    const unsigned char* kv = (const unsigned char*)a.kv;
+    RowResolver rr{a.block_table, a.cache_seqlens, nullptr, a.s_q, a.max_blocks, 0, a.causal, a.num_rows};
+
+    const int lds_tiles = (int)(size_t)(lds_void_t*)&sm.tile[0][0];
+
+    // One segment = the tiles of item j that this partition holds.  Every role
+    // walks the same segments and passes the same barriers (n + 5 per segment).
+    struct Seg {
+        int nslots, g0, n, slot, b, iq;
+        bool final_out, write_ok;
+    };
+    auto segment = [&](int j, Seg& sg) __attribute__((always_inline)) -> bool {
+        sg.nslots = rr.slots_uniform(j);
+        const int ntile_j = (sg.nslots + 63) >> 6;
+        const int t0 = (j == jb && tbeg > 0) ? tbeg : 0;
+        int t1 = (j == je) ? tend : ntile_j;
+        if (t1 > ntile_j) t1 = ntile_j;
+        if (t0 >= t1) return false;
+        const int nsplit = sload(so + j + 1) - sload(so + j);
+        sg.slot = (j == jb) ? slot0 : sload(so + j);
+        sg.g0 = 2 * t0;                                                     // first 32-token tile
+        sg.n = min(2 * t1, (sg.nslots + kSubTok - 1) / kSubTok) - sg.g0;   // tiles of this segment
+        sg.final_out = nsplit == 1;
+        sg.write_ok = sg.final_out || (sg.slot >= 0 && sg.slot < a.max_slots);
+        sg.b = j / a.s_q;
+        sg.iq = j - sg.b * a.s_q;
+        return true;
+    };
+
+    if (is_copy) {
+        // -------------------------------------------------------------------- copy waves
+        for (int j = jb; j <= je && j < N; ++j) {
+            Seg sg;
+            if (!segment(j, sg)) continue;
+            const int npages_item = (sg.nslots + kBlock - 1) / kBlock;
+            int pt_base = 0, pt_v = 0;
+            auto load_pages = [&](int first) __attribute__((always_inline)) {
+                pt_base = first;
+                const int pi = first + lane_id64();
+                pt_v = pi < npages_item ? a.block_table[(int64_t)sg.b * a.max_blocks + pi] : 0;
+                __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
+            };
+            load_pages(sg.g0 >> 1);
+            // A tile is copied as 36 blocks of 1 KiB, block 4 cg + tg holding the
+            // 128-byte line cg (columns 8 cg .. 8 cg + 7) of tokens 8 tg .. 8 tg + 7,
+            // so that every copy instruction reads eight whole lines (see
+            // tile_chunk).  Copy wave cw copies token groups 2 cw and 2 cw + 1
+            // (18 blocks): one wave sustains about 1 KiB of direct-to-LDS loads
+            // per 90 cycles, so both copy waves share every tile.  Lane l copies
+            // token 8 tg + l / 8, column 8 cg + ((l % 8) ^ swz(token)); the byte
+            // count of the buffer of token group tg stops at the valid tokens,
+            // so the rest land as zeros.
+            auto copy_tile = [&](int it) __attribute__((always_inline)) {
+                const int g = sg.g0 + it;
+                if (((g >> 1) - pt_base) >= 64) load_pages(g >> 1);
+                const int page = __builtin_amdgcn_readlane(pt_v, (g >> 1) - pt_base);
+                const bool ok = page_ok(page, a.num_rows);
+                int nvalid = min(sg.nslots - g * kSubTok, kSubTok);
+                if (!ok || nvalid < 0) nvalid = 0;
+                const unsigned char* base = kv + (ok ? (int64_t)page * kTileBytes + (g & 1) * kTileB : 0);
+                const int dst = lds_tiles + ring_offset(it % kRing);
+                const int ln = lane_id64();
+                const int tq = ln >> 3, sl = ln & 7;
+                const int fbe = tq * kRowBytes + 16 * (sl ^ tq);         // even token groups: swz = tq
+                const int fbo = tq * kRowBytes + 16 * (sl ^ tq ^ 1);     // odd token groups: swz = tq ^ 1
+                unroll<0, 2>([&](auto u_c) __attribute__((always_inline)) {
+                    constexpr int u = decltype(u_c)::value;
+                    const int tg = 2 * cw + u;
+                    i32x4 rs = rsrc(base + 8 * tg * kRowBytes, min(max(nvalid - 8 * tg, 0), 8) * kRowBytes);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) rs[e] = __builtin_amdgcn_readfirstlane(rs[e]);   // uniform by construction
+                    unroll<0, 9>([&](auto cg_c) __attribute__((always_inline)) {
+                        constexpr int cg = decltype(cg_c)::value;
+                        copy_x4<128 * cg>(rs, u ? fbo : fbe, dst + 1024 * (4 * cg + tg));
+                    });
+                });
+                if (cw == 0) sm.valid[it % kRing] = nvalid;
+            };
+            // L2 prefetch of tile it: one 4-byte load per 128-byte line (lines
+            // 144 cw .. 144 cw + 143 of the 288) into a sink in LDS that nothing
+            // reads.  Always three instructions, issued after a step's copies, so
+            // that the wait for those copies is vmcnt(3) (loads complete in issue
+            // order) and a prefetch has a whole step to arrive.
+            const int sink = (int)(size_t)(lds_void_t*)&sm.pf_sink[0];
+            auto prefetch_tile = [&](int it) __attribute__((always_inline)) {
+                const int g = sg.g0 + it;
+                int nbytes = 0;
+                const unsigned char* base = kv;
+                // a page past the window of page ids is not prefetched: the
+                // window is moved only by the copies, which still need it
+                if (it < sg.n && ((g >> 1) - pt_base) < 64) {
+                    const int page = __builtin_amdgcn_readlane(pt_v, (g >> 1) - pt_base);
+                    if (page_ok(page, a.num_rows)) {
+                        nbytes = max(0, min(sg.nslots - g * kSubTok, kSubTok)) * kRowBytes;
+                        base = kv + (int64_t)page * kTileBytes + (g & 1) * kTileB;
+                    }
+                }
+                const int lo = 128 * (144 * cw + lane_id64());
+                const int hi = 144 * 128 * (cw + 1);       // this wave's lines end here
+                i32x4 rs = rsrc(base, min(nbytes, hi));
+#pragma unroll
+                for (int e = 0; e < 4; ++e) rs[e] = __builtin_amdgcn_readfirstlane(rs[e]);   // uniform by construction
+                prefetch_x1(rs, lo, sink);
+                prefetch_x1(rs, lo + 8192, sink);
+                prefetch_x1(rs, lo + 16384, sink);
+            };
+            constexpr int kLead = 4;    // step k copies tile k + 2 and prefetches tile k + kLead
+            copy_tile(0);
+#pragma unroll
+            for (int it = 1; it < kLead - 1; ++it) prefetch_tile(it);
+            __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): tile 0 has landed
+            barrier_lds();
+            for (int k = -1; k <= sg.n; ++k) {
+                if (k + 2 < sg.n) {
+                    copy_tile(k + 2);
+                    prefetch_tile(k + kLead);
+                    __builtin_amdgcn_s_waitcnt(0x0F73);   // vmcnt(3): this wave's copies have landed
+                } else {
+                    __builtin_amdgcn_s_waitcnt(0x0F70);
+                }
+                barrier_lds();
+            }
+            __builtin_amdgcn_s_waitcnt(0x0F70);   // every load of this wave has written LDS
+            barrier_lds();   // epilogue
+            barrier_lds();   // the next segment reuses every LDS array
+        }
+    } else if (is_qk) {
+        // -------------------------------------------------------------------- QK waves
+        for (int j = jb; j <= je && j < N; ++j) {
+            Seg sg;
+            if (!segment(j, sg)) continue;
+            const int ln = lane_id64();
+            const int h32 = ln & 31, hf = ln >> 5;
+            const int head = hblk * kH + hbq * 32 + h32;
+            const bool head_ok = head < H;
+            bf16x8 qf[36];
+            {
+                const bf16x8* qp = (const bf16x8*)((const unsigned char*)a.q +
+                                                   ((int64_t)j * H + (head_ok ? head : 0)) * kRowBytes);
+#pragma unroll
+                for (int kk = 0; kk < 36; ++kk) {
+                    bf16x8 v = qp[2 * kk + hf];
+                    if (!head_ok) v = bf16x8{};
+                    qf[kk] = v;
+                }
+            }
+            float m_run = -INFINITY, l_run = 0.f;
+            f32x16 s = {}, sa = {}, sb = {};
+            barrier_lds();   // tile 0 has landed
+
+            // Softmax of the tile whose scores are in s, in stages that run
+            // between the MFMAs of the next tile's QK (stage st after MFMA st):
+            // tile max, the exact running max (raised when the tile max exceeds
+            // it by more than tau in log2 units; tau = 0: whenever it is
+            // larger), alpha, p = exp2(s c - m c) one score per stage, l, then
+            // P rounded to bf16 and published with alpha.
+            float mxa = 0.f, mxb = 0.f, m_new = 0.f, cm = 0.f, alpha = 0.f, psum = 0.f;
+            bf16x8 p0 = {}, p1 = {};
+            constexpr int kSoftStages = 27;
+            auto soft_stage = [&](auto st_c, int tslot) __attribute__((always_inline)) {
+                constexpr int st = decltype(st_c)::value;
+                if constexpr (st == 0) {
+                    mxa = fmaxf(fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3])), fmaxf(fmaxf(s[4], s[5]), fmaxf(s[6], s[7])));
+                } else if constexpr (st == 1) {
+                    mxb = fmaxf(fmaxf(fmaxf(s[8], s[9]), fmaxf(s[10], s[11])), fmaxf(fmaxf(s[12], s[13]), fmaxf(s[14], s[15])));
+                } else if constexpr (st == 2) {
+                    mxa = wave_max_pair(fmaxf(mxa, mxb));   // the two lanes of a head hold disjoint tokens
+                } else if constexpr (st == 3) {
+                    m_new = c * (mxa - m_run) <= a.rescale_tau ? m_run : fmaxf(m_run, mxa);
+                    cm = m_new == -INFINITY ? 0.f : c * m_new;
+                } else if constexpr (st == 4) {
+                    alpha = __builtin_amdgcn_exp2f(c * m_run - cm);
+                } else if constexpr (st >= 5 && st < 21) {
+                    constexpr int r = st - 5;
+                    s[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c, -cm));
+                } else if constexpr (st == 21) {
+                    psum = ((s[0] + s[1]) + (s[2] + s[3])) + ((s[4] + s[5]) + (s[6] + s[7]));
+                } else if constexpr (st == 22) {
+                    psum += ((s[8] + s[9]) + (s[10] + s[11])) + ((s[12] + s[13]) + (s[14] + s[15]));
+                } else if constexpr (st == 23) {
+                    psum = wave_sum_pair(psum);
+                    l_run = l_run * alpha + psum;
+                    m_run = m_new;
+                } else if constexpr (st == 24) {
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) p0[e] = (__bf16)s[e];
+                } else if constexpr (st == 25) {
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) p1[e] = (__bf16)s[8 + e];
+                } else if constexpr (st == 26) {
+                    const int l = lane_id64();
+                    sm.p[tslot][hbq][0][l] = p0;
+                    sm.p[tslot][hbq][1][l] = p1;
+                    sm.alpha[tslot][hbq][l & 31] = alpha;   // both lanes of a head write the same value
+                }
+            };
+            // QK(t): S^T = K Q^T over 36 k-steps, even k-steps into sa and odd
+            // ones into sb, K fragments read kQkLA ahead.  The order is fixed
+            // with scheduling fences: MFMA i, the read of fragment i + kQkLA,
+            // then softmax stage i of the previous tile when SOFT.
+            auto qk = [&](int t, auto soft_c, int tslot) __attribute__((always_inline)) {
+                constexpr bool SOFT = decltype(soft_c)::value != 0;
+                // K operand of k-step kk: token l % 32, column 2 kk + half; its
+                // byte offset is 4096 (kk / 4) plus a lane term kb[kk % 4]
+                const unsigned char* T = sm.tile[0] + ring_offset(t % kRing);
+                int kb[4];
+                {
+                    const int l = lane_id64();
+                    const int tk = l & 31, hl = l >> 5;
+#pragma unroll
+                    for (int m = 0; m < 4; ++m) kb[m] = tile_chunk(tk, 2 * m + hl) * 16;
+                }
+                bf16x8 fr[kQkLA + 1];
+#pragma unroll
+                for (int i = 0; i < kQkLA; ++i) fr[i] = *(const bf16x8*)(T + 4096 * (i >> 2) + kb[i & 3]);
+                __builtin_amdgcn_sched_barrier(0);
+                unroll<0, 36>([&](auto i_c) __attribute__((always_inline)) {
+                    constexpr int i = decltype(i_c)::value;
+                    const bf16x8 A = fr[i % (kQkLA + 1)];
+                    if constexpr (i == 0) sa = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, qf[0], f32x16{}, 0, 0, 0);
+                    else if constexpr (i == 1) sb = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, qf[1], f32x16{}, 0, 0, 0);
+                    else if constexpr (i & 1) sb = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, qf[i], sb, 0, 0, 0);
+                    else sa = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, qf[i], sa, 0, 0, 0);
+                    if constexpr (i + kQkLA < 36)
+                        fr[(i + kQkLA) % (kQkLA + 1)] = *(const bf16x8*)(T + 4096 * ((i + kQkLA) >> 2) + kb[(i + kQkLA) & 3]);
+                    if constexpr (SOFT && i < kSoftStages) soft_stage(Int<i>{}, tslot);
+                    __builtin_amdgcn_sched_barrier(0);
+                });
+            };
+            // the scores of tile t into s, masked tokens (8 (r / 4) + 4 half + r % 4) at -inf
+            auto scores = [&](int t) __attribute__((always_inline)) {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) s[r] = sa[r] + sb[r];
+                const int nv = __builtin_amdgcn_readfirstlane(sm.valid[t % kRing]);
+                if (nv < kSubTok) {
+                    const int h4 = 4 * (lane_id64() >> 5);
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const int c_r = 8 * (r >> 2) + (r & 3);
+                        if (!(h4 < nv - c_r)) s[r] = -INFINITY;
+                    }
+                }
+            };
+            // step -1: QK(0)
+            qk(0, Int<0>{}, 0);
+            barrier_lds();
+            // steps 0 .. n-2: softmax(k) and QK(k+1)
+            for (int k = 0; k + 1 < sg.n; ++k) {
+                scores(k);
+                qk(k + 1, Int<1>{}, k & 1);
+                barrier_lds();
+            }
+            // step n-1: the last softmax, then the output scale and lse
+            {
+                const int k = sg.n - 1;
+                scores(k);
+                unroll<0, kSoftStages>([&](auto st_c) __attribute__((always_inline)) { soft_stage(st_c, k & 1); });
+                const int l = lane_id64();
+                const int hd = hblk * kH + hbq * 32 + (l & 31);
+                const float lse_v = l_run > 0.f ? (c * m_run + log2f(l_run)) * 0.69314718055994531f
+                                                 : (l_run == 0.f ? -INFINITY : __builtin_nanf(""));
+                float inv = l_run > 0.f ? 1.f / l_run : 0.f;
+                if (sg.final_out && a.attn_sink && hd < H) inv *= 1.f / (1.f + __expf(a.attn_sink[hd] - lse_v));
+                sm.fin_inv[hbq * 32 + (l & 31)] = inv;
+                if (l < 32 && hd < H && sg.write_ok) {
+                    if (sg.final_out) a.lse[((int64_t)sg.b * H + hd) * a.s_q + sg.iq] = lse_v;
+                    else a.lse_part[(int64_t)sg.slot * H + hd] = lse_v;
+                }
+                barrier_lds();
+            }
+            barrier_lds();   // step n
+            barrier_lds();   // epilogue
+            barrier_lds();   // the next segment reuses every LDS array
+        }
+    } else {
+        // -------------------------------------------------------------------- PV waves
+        for (int j = jb; j <= je && j < N; ++j) {
+            Seg sg;
+            if (!segment(j, sg)) continue;
+            // acc[hb][d], register r, lane l: head 32 hb + l % 32, dim 128 dq +
+            // 32 d + 8 (r / 4) + 4 half + r % 4
+            f32x16 acc[2][4];
+#pragma unroll
+            for (int hb = 0; hb < 2; ++hb)
+#pragma unroll
+                for (int d = 0; d < 4; ++d) acc[hb][d] = f32x16{};
+            barrier_lds();   // tile 0 has landed
+            barrier_lds();   // step -1
+            barrier_lds();   // step 0
+            // PV(t): O^T += V^T P^T for the four 32-dim blocks of this wave's
+            // quarter and both head blocks; each block is rescaled by alpha
+            // before its first MFMA, the multiplies of block d + 1 placed between
+            // the MFMAs of block d.  V fragments are read kPvLA ahead; the order
+            // is fixed with scheduling fences.
+            auto pv = [&](int t, float al0, float al1, bool rescale, const bf16x8 (&P)[2][2]) __attribute__((always_inline)) {
+                // V^T operand (transposed read): lane (gq = l / 16, i16 = l % 16)
+                // reads 8 bytes (byte 8 (i16 % 2) of the 16-byte chunk) of token
+                // 16 ks + 8 r + 4 (gq / 2) + i16 / 4 and column 16 dq + 4 d + 2 (gq % 2)
+                // + (i16 % 4) / 2, r = 0, 1 for the two reads of a fragment.  The
+                // byte offset is 8192 dq + 4096 (d / 2) + 2048 ks plus a lane term
+                // vb[d % 2][r].
+                int vb[2][2];
+                {
+                    const int l = lane_id64();
+                    const int gq = l >> 4, i16 = l & 15;
+                    const int x = 2 * (gq & 1) + ((i16 & 3) >> 1);
+                    const int tq = 4 * (gq >> 1) + (i16 >> 2);
+#pragma unroll
+                    for (int e = 0; e < 2; ++e)
+#pragma unroll
+                        for (int r = 0; r < 2; ++r) vb[e][r] = tile_chunk(8 * r + tq, 4 * e + x) * 16 + 8 * (i16 & 1);
+                }
+                const unsigned char* T = sm.tile[0] + ring_offset(t % kRing) + 8192 * dq;
+                bf16x8 fr[kPvLA + 1];
+                auto fetch = [&](int i) __attribute__((always_inline)) -> bf16x8 {
+                    const int d = i >> 1, ks = i & 1;
+                    const unsigned char* Tv = T + 4096 * (d >> 1) + 2048 * ks;
+                    const bf16x4 v0 = tr_read64(Tv + vb[d & 1][0]);
+                    const bf16x4 v1 = tr_read64(Tv + vb[d & 1][1]);
+                    return bf16x8{v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+                };
+#pragma unroll
+                for (int i = 0; i < kPvLA; ++i) fr[i] = fetch(i);
+                if (rescale) {
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) { acc[0][0][r] *= al0; acc[1][0][r] *= al1; }
+                }
+                __builtin_amdgcn_sched_barrier(0);
+                unroll<0, 8>([&](auto i_c) __attribute__((always_inline)) {
+                    constexpr int i = decltype(i_c)::value;      // fragment (dim block i / 2, k-step i % 2)
+                    constexpr int d = i >> 1, ks = i & 1;
+                    const bf16x8 A = fr[i % (kPvLA + 1)];
+                    acc[0][d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, P[0][ks], acc[0][d], 0, 0, 0);
+                    if constexpr (d + 1 < 4) {
+                        if (rescale) {
+#pragma unroll
+                            for (int r = 0; r < 8; ++r) acc[ks][d + 1][r] *= ks ? al1 : al0;
+                        }
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
+                    acc[1][d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, P[1][ks], acc[1][d], 0, 0, 0);
+                    if constexpr (d + 1 < 4) {
+                        if (rescale) {
+#pragma unroll
+                            for (int r = 8; r < 16; ++r) acc[ks][d + 1][r] *= ks ? al1 : al0;
+                        }
+                    }
+                    if constexpr (i + kPvLA < 8) fr[(i + kPvLA) % (kPvLA + 1)] = fetch(i + kPvLA);
+                    __builtin_amdgcn_sched_barrier(0);
+                });
+            };
+            for (int k = 1; k <= sg.n; ++k) {
+                const int t = k - 1, ts = t & 1;
+                const int l = lane_id64();
+                bf16x8 P[2][2];
+#pragma unroll
+                for (int hb = 0; hb < 2; ++hb)
+#pragma unroll
+                    for (int ks = 0; ks < 2; ++ks) P[hb][ks] = sm.p[ts][hb][ks][l];
+                const float al0 = sm.alpha[ts][0][l & 31], al1 = sm.alpha[ts][1][l & 31];
+                // the rescale is skipped when no head's max rose (alpha = 1 for all)
+                const bool rescale = __builtin_amdgcn_ballot_w64(al0 != 1.f || al1 != 1.f) != 0;
+                pv(t, al0, al1, rescale, P);
+                barrier_lds();
+            }
+            barrier_lds();   // epilogue: fin_inv was written in step n - 1
+            // ---- epilogue: normalise and store
+            if (sg.write_ok) {
+                const int l = lane_id64();
+                const int hf = l >> 5;
+#pragma unroll
+                for (int hb = 0; hb < 2; ++hb) {
+                    const int head = hblk * kH + hb * 32 + (l & 31);
+                    if (head >= H) continue;
+                    const float inv = sm.fin_inv[hb * 32 + (l & 31)];
+                    const bool part16 = !sg.final_out && a.part_fp16;
+                    int E = 0;
+                    if (part16) {
+                        float amax = 0.f;
+#pragma unroll
+                        for (int d = 0; d < 4; ++d)
+#pragma unroll
+                            for (int r = 0; r < 16; ++r) amax = fmaxf(amax, fabsf(acc[hb][d][r]));
+                        amax *= inv;
+                        const int be = (int)((__float_as_uint(amax) >> 23) & 0xff);
+                        E = amax > 0.f ? (be == 0 ? -125 : be - 126) : 0;        // amax * 2^-E < 1
+                        E = E > 127 ? 127 : E;
+                        a.o_exp8[((int64_t)sg.slot * H + head) * 8 + 2 * dq + hf] = (unsigned char)(signed char)E;
+                    }
+#pragma unroll
+                    for (int d = 0; d < 4; ++d) {
+#pragma unroll
+                        for (int rq = 0; rq < 4; ++rq) {
+                            const int dim = 128 * dq + 32 * d + 8 * rq + 4 * hf;
+                            const float v0 = acc[hb][d][4 * rq + 0] * inv, v1 = acc[hb][d][4 * rq + 1] * inv;
+                            const float v2 = acc[hb][d][4 * rq + 2] * inv, v3 = acc[hb][d][4 * rq + 3] * inv;
+                            if (part16) {
+                                const int64_t o = ((int64_t)sg.slot * H + head) * kDv + dim;
+                                typedef __attribute__((__vector_size__(4 * sizeof(_Float16)))) _Float16 f16x4;
+                                *(f16x4*)((_Float16*)a.o_part + o) = f16x4{(_Float16)ldexpf(v0, -E), (_Float16)ldexpf(v1, -E),
+                                                                             (_Float16)ldexpf(v2, -E), (_Float16)ldexpf(v3, -E)};
+                            } else if (sg.final_out) {
+                                const int64_t o = ((int64_t)j * H + head) * kDv + dim;
+                                if (a.out_fp32) *(f32x4*)((float*)a.out + o) = f32x4{v0, v1, v2, v3};
+                                else *(bf16x4*)((__bf16*)a.out + o) = bf16x4{(__bf16)v0, (__bf16)v1, (__bf16)v2, (__bf16)v3};
+                            } else {
+                                const int64_t o = ((int64_t)sg.slot * H + head) * kDv + dim;
+                                *(f32x4*)(a.o_part + o) = f32x4{v0, v1, v2, v3};
+                            }
+                        }
+                    }
+                }
+            }
+            barrier_lds();   // the next segment reuses every LDS array
+        }
+    }
+}
+
+hipError_t launch_decode64(const DecodeArgs& a, hipStream_t stream) {
+    hipLaunchKernelGGL(decode64_kernel, dim3(a.num_parts * a.n_hblk), dim3(kT), 0, stream, a);
+    return hipGetLastError();
+}
+
+}  // namespace mla

@@ -17,8 +17,9 @@ struct DecodeArgs {
     const int32_t* meta;         // scheduler metadata (device)
     float* o_part;               // [max_slots, H, 512] float32, or float16 when part_fp16
     float* lse_part;             // [max_slots, H]
-    uint32_t* o_exp;             // part_fp16: [max_slots, H] four int8 power-of-two scales per head
-    int part_fp16;               // split partials stored as scaled float16 (see the decode epilogue)
+    unsigned char* o_exp8;       // part_fp16: [max_slots, H, 8] int8 power-of-two exponents; byte 2 q + h
+                                 // scales dims d with d / 128 = q and (d % 8) / 4 = h
+    int part_fp16;               // split partials stored as scaled float16 (see the decode epilogues)
     void* out;                   // [B, S, H, 512]
     float* lse;                  // [B, H, S]
     int64_t num_rows;            // num_blocks * 64
@@ -35,9 +36,9 @@ struct MetaArgs {
 };
 
 struct CombineArgs {
-    const float* o_part;         // float32, or float16 with o_exp scales when part_fp16
+    const float* o_part;         // float32, or float16 with o_exp8 exponents when part_fp16
     const float* lse_part;
-    const uint32_t* o_exp;
+    const unsigned char* o_exp8;
     int part_fp16;
     const int32_t* split_offsets;
     const float* attn_sink;      // [H] or null
@@ -57,6 +58,8 @@ struct GatherArgs {
 // kvf: 0 = bf16 rows of 576, 1 = 656-byte FP8 records, 2 = 528-byte FP8 records, 3 = 288-byte FP4 records
 // (2 and 3: 512-wide head, sparse only)
 hipError_t launch_decode(const DecodeArgs& a, bool sparse, int kvf, hipStream_t stream);
+// dense bf16 cache, 64 heads per workgroup (num_head_blocks = ceil(h_q / 64))
+hipError_t launch_decode64(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_metadata(const MetaArgs& a, hipStream_t stream);
 hipError_t launch_combine(const CombineArgs& a, hipStream_t stream);
 hipError_t launch_gather(const GatherArgs& a, hipStream_t stream);

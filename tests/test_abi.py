@@ -35,7 +35,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_abi_version_and_status_strings(lib):
-    assert lib.mla_abi_version() == 2
+    assert lib.mla_abi_version() == 3
     for s in range(6):
         assert lib.mla_status_string(s)
     assert lib.mla_status_string(99) == b"unknown status"
@@ -51,17 +51,23 @@ def _problem(**kw):
 
 def test_plan_host_only():
     import mla_decode_amd as mla
+    # dense decode over a bf16 cache: 64 heads per workgroup
     m = mla.plan(_problem(), num_cus=256)
-    assert m.num_head_blocks == 1 and m.num_partitions == 256 and m.fixed_overhead == 0
-    assert m.max_splits == 64 + 256
-    assert m.bytes == (8 + 5 * 256 + 64 + 1) * 4
-    assert mla.workspace_bytes(m) == 320 * 128 * 513 * 4
+    assert m.num_head_blocks == 2 and m.num_partitions == 128 and m.fixed_overhead == 0
+    assert m.max_splits == 64 + 128
+    assert m.bytes == (8 + 5 * 128 + 64 + 1) * 4
+    assert mla.workspace_bytes(m) == 192 * 128 * 513 * 4
     m = mla.plan(_problem(h_q=192), num_cus=256)
-    assert m.num_head_blocks == 2 and m.num_partitions == 128
+    assert m.num_head_blocks == 3 and m.num_partitions == 85
     m = mla.plan(_problem(h_q=16, batch=2, num_blocks=8, max_blocks_per_seq=4), num_cus=256)
     assert m.num_head_blocks == 1 and m.num_partitions == 256
+    # other formats and top-k problems: 128 heads per workgroup
+    m = mla.plan(_problem(kv_format="fp8"), num_cus=256)
+    assert m.num_head_blocks == 1 and m.num_partitions == 256
+    m = mla.plan(_problem(h_q=192, topk=2048), num_cus=256)
+    assert m.num_head_blocks == 2 and m.num_partitions == 128
     for tau in (0.0, 6.0, 8.0, 30.0):   # lazy-rescale thresholds in range
-        assert mla.plan(_problem(rescale_threshold=tau), num_cus=256).num_partitions == 256
+        assert mla.plan(_problem(rescale_threshold=tau), num_cus=256).num_partitions == 128
 
 
 def test_struct_layout_matches_header():
