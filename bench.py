@@ -490,6 +490,10 @@ def main():
                     help="dense_b64_s4096 (= config2) is the headline line; see the module docstring")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a 1 GiB device copy 5 times (reference for HBM byte counters)")
+    ap.add_argument("--kernel-only", type=int, default=0, metavar="N",
+                    help="profiling mode: build the workload, run the scheduler once, then launch only the "
+                         "partial-attention kernel N times in the step's own partial format (for counter runs "
+                         "whose dispatches are all production launches)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (the decode path has no multi-GPU code); got --gpus {args.gpus}",
@@ -505,9 +509,31 @@ def main():
         torch.cuda.synchronize()
         print(json.dumps({"copy_bytes_per_launch": n, "launches": 5}), flush=True)
         return
+    if args.kernel_only:
+        return kernel_only(args)
     if args.workload == "sparse_prefill":
         return bench_prefill(args)
     return bench_decode(args)
+
+
+def kernel_only(args):
+    """The partial-attention kernel alone, ``--kernel-only`` times after the
+    warm-up, in the launch configuration the decode step uses."""
+    import torch
+    import mla_decode_amd as mla
+    dev = torch.device("cuda:0")
+    w = load_workload(args.workload if args.workload != "sparse_prefill" else "config4", dev)
+    dec = mla.Decoder.for_workload(w, dev)
+    stream = torch.cuda.current_stream(dev)
+    dec.metadata(None if w.topk else w.cache_seqlens, stream)
+
+    def k():
+        dec.decode_partial(w.q, w.kv, w.block_table, w.cache_seqlens, w.indices, stream, production=True)
+
+    nwarm, _ = _warmup(k, args.warmup)
+    ms, per = _timed(k, args.kernel_only, stream)
+    print(json.dumps({"workload": args.workload, "launches": args.kernel_only, "warmup_launches": nwarm,
+                      "us_per_launch": round(ms * 1e3, 2), "us_p50": round(_pct(per, 50) * 1e3, 2)}), flush=True)
 
 
 if __name__ == "__main__":

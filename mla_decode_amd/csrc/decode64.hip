@@ -382,7 +382,7 @@ __global__ void __launch_bounds__(kT, 1) decode64_kernel(const DecodeArgs a) {
             // ones into sb, K fragments read kQkLA ahead.  The order is fixed
             // with scheduling fences: MFMA i, the read of fragment i + kQkLA,
             // then softmax stage i of the previous tile when SOFT.
-            auto qk = [&](int t, auto soft_c, int tslot) __attribute__((always_inline)) {
+            auto qk = [&](int t, auto soft_c, int tslot, auto&& pre) __attribute__((always_inline)) {
                 constexpr bool SOFT = decltype(soft_c)::value != 0;
                 // K operand of k-step kk: token l % 32, column 2 kk + half; its
                 // byte offset is 4096 (kk / 4) plus a lane term kb[kk % 4]
@@ -398,6 +398,8 @@ __global__ void __launch_bounds__(kT, 1) decode64_kernel(const DecodeArgs a) {
 #pragma unroll
                 for (int i = 0; i < kQkLA; ++i) fr[i] = *(const bf16x8*)(T + 4096 * (i >> 2) + kb[i & 3]);
                 __builtin_amdgcn_sched_barrier(0);
+                pre();   // runs while the first fragments are in flight
+                __builtin_amdgcn_sched_barrier(0);
                 unroll<0, 36>([&](auto i_c) __attribute__((always_inline)) {
                     constexpr int i = decltype(i_c)::value;
                     const bf16x8 A = fr[i % (kQkLA + 1)];
@@ -411,11 +413,11 @@ __global__ void __launch_bounds__(kT, 1) decode64_kernel(const DecodeArgs a) {
                     __builtin_amdgcn_sched_barrier(0);
                 });
             };
-            // the scores of tile t into s, masked tokens (8 (r / 4) + 4 half + r % 4) at -inf
-            auto scores = [&](int t) __attribute__((always_inline)) {
+            // the scores of a tile into s, masked tokens (8 (r / 4) + 4 half + r % 4)
+            // at -inf; nv = its valid token count
+            auto scores = [&](int nv) __attribute__((always_inline)) {
 #pragma unroll
                 for (int r = 0; r < 16; ++r) s[r] = sa[r] + sb[r];
-                const int nv = __builtin_amdgcn_readfirstlane(sm.valid[t % kRing]);
                 if (nv < kSubTok) {
                     const int h4 = 4 * (lane_id64() >> 5);
 #pragma unroll
@@ -425,19 +427,25 @@ __global__ void __launch_bounds__(kT, 1) decode64_kernel(const DecodeArgs a) {
                     }
                 }
             };
+            // The valid token count of tile k is written with its copy in step
+            // k - 2 and read in step k - 1, so no step starts with a wait for it.
+            auto valid_of = [&](int t) __attribute__((always_inline)) -> int {
+                return __builtin_amdgcn_readfirstlane(sm.valid[t % kRing]);
+            };
             // step -1: QK(0)
-            qk(0, Int<0>{}, 0);
+            qk(0, Int<0>{}, 0, [] {});
+            int nv = valid_of(0);
             barrier_lds();
             // steps 0 .. n-2: softmax(k) and QK(k+1)
             for (int k = 0; k + 1 < sg.n; ++k) {
-                scores(k);
-                qk(k + 1, Int<1>{}, k & 1);
+                qk(k + 1, Int<1>{}, k & 1, [&] { scores(nv); });
+                nv = valid_of(k + 1);
                 barrier_lds();
             }
             // step n-1: the last softmax, then the output scale and lse
             {
                 const int k = sg.n - 1;
-                scores(k);
+                scores(nv);
                 unroll<0, kSoftStages>([&](auto st_c) __attribute__((always_inline)) { soft_stage(st_c, k & 1); });
                 const int l = lane_id64();
                 const int hd = hblk * kH + hbq * 32 + (l & 31);
@@ -470,48 +478,51 @@ __global__ void __launch_bounds__(kT, 1) decode64_kernel(const DecodeArgs a) {
                 for (int d = 0; d < 4; ++d) acc[hb][d] = f32x16{};
             barrier_lds();   // tile 0 has landed
             barrier_lds();   // step -1
-            barrier_lds();   // step 0
+            // V^T operand (transposed read): lane (gq = l / 16, i16 = l % 16)
+            // reads 8 bytes (byte 8 (i16 % 2) of the 16-byte chunk) of token
+            // 16 ks + 8 r + 4 (gq / 2) + i16 / 4 and column 16 dq + 4 d + 2 (gq % 2)
+            // + (i16 % 4) / 2, r = 0, 1 for the two reads of a fragment.  The
+            // byte offset is 8192 dq + 4096 (d / 2) + 2048 ks plus a lane term
+            // vb[d % 2][r].
+            int vb[2][2];
+            {
+                const int l = lane_id64();
+                const int gq = l >> 4, i16 = l & 15;
+                const int x = 2 * (gq & 1) + ((i16 & 3) >> 1);
+                const int tq = 4 * (gq >> 1) + (i16 >> 2);
+#pragma unroll
+                for (int e = 0; e < 2; ++e)
+#pragma unroll
+                    for (int r = 0; r < 2; ++r) vb[e][r] = tile_chunk(8 * r + tq, 4 * e + x) * 16 + 8 * (i16 & 1);
+            }
+            // fragment i = (dim block i / 2, k-step i % 2) of tile t, ring slot i % (kPvLA + 1)
+            bf16x8 fr[kPvLA + 1];
+            auto fetch = [&](int t, int i) __attribute__((always_inline)) -> bf16x8 {
+                const int d = i >> 1, ks = i & 1;
+                const unsigned char* Tv = sm.tile[0] + ring_offset(t % kRing) + 8192 * dq + 4096 * (d >> 1) + 2048 * ks;
+                const bf16x4 v0 = tr_read64(Tv + vb[d & 1][0]);
+                const bf16x4 v1 = tr_read64(Tv + vb[d & 1][1]);
+                return bf16x8{v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+            };
+            // the first fragments of tile t, read in the step before its PV (tile t
+            // is resident from step t - 1 to step t + 1)
+            auto prefetch = [&](int t) __attribute__((always_inline)) {
+#pragma unroll
+                for (int i = 0; i < kPvLA; ++i) fr[i] = fetch(t, i);
+            };
             // PV(t): O^T += V^T P^T for the four 32-dim blocks of this wave's
             // quarter and both head blocks; each block is rescaled by alpha
             // before its first MFMA, the multiplies of block d + 1 placed between
             // the MFMAs of block d.  V fragments are read kPvLA ahead; the order
             // is fixed with scheduling fences.
             auto pv = [&](int t, float al0, float al1, bool rescale, const bf16x8 (&P)[2][2]) __attribute__((always_inline)) {
-                // V^T operand (transposed read): lane (gq = l / 16, i16 = l % 16)
-                // reads 8 bytes (byte 8 (i16 % 2) of the 16-byte chunk) of token
-                // 16 ks + 8 r + 4 (gq / 2) + i16 / 4 and column 16 dq + 4 d + 2 (gq % 2)
-                // + (i16 % 4) / 2, r = 0, 1 for the two reads of a fragment.  The
-                // byte offset is 8192 dq + 4096 (d / 2) + 2048 ks plus a lane term
-                // vb[d % 2][r].
-                int vb[2][2];
-                {
-                    const int l = lane_id64();
-                    const int gq = l >> 4, i16 = l & 15;
-                    const int x = 2 * (gq & 1) + ((i16 & 3) >> 1);
-                    const int tq = 4 * (gq >> 1) + (i16 >> 2);
-#pragma unroll
-                    for (int e = 0; e < 2; ++e)
-#pragma unroll
-                        for (int r = 0; r < 2; ++r) vb[e][r] = tile_chunk(8 * r + tq, 4 * e + x) * 16 + 8 * (i16 & 1);
-                }
-                const unsigned char* T = sm.tile[0] + ring_offset(t % kRing) + 8192 * dq;
-                bf16x8 fr[kPvLA + 1];
-                auto fetch = [&](int i) __attribute__((always_inline)) -> bf16x8 {
-                    const int d = i >> 1, ks = i & 1;
-                    const unsigned char* Tv = T + 4096 * (d >> 1) + 2048 * ks;
-                    const bf16x4 v0 = tr_read64(Tv + vb[d & 1][0]);
-                    const bf16x4 v1 = tr_read64(Tv + vb[d & 1][1]);
-                    return bf16x8{v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
-                };
-#pragma unroll
-                for (int i = 0; i < kPvLA; ++i) fr[i] = fetch(i);
                 if (rescale) {
 #pragma unroll
                     for (int r = 0; r < 16; ++r) { acc[0][0][r] *= al0; acc[1][0][r] *= al1; }
                 }
                 __builtin_amdgcn_sched_barrier(0);
                 unroll<0, 8>([&](auto i_c) __attribute__((always_inline)) {
-                    constexpr int i = decltype(i_c)::value;      // fragment (dim block i / 2, k-step i % 2)
+                    constexpr int i = decltype(i_c)::value;
                     constexpr int d = i >> 1, ks = i & 1;
                     const bf16x8 A = fr[i % (kPvLA + 1)];
                     acc[0][d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, P[0][ks], acc[0][d], 0, 0, 0);
@@ -529,10 +540,12 @@ __global__ void __launch_bounds__(kT, 1) decode64_kernel(const DecodeArgs a) {
                             for (int r = 8; r < 16; ++r) acc[ks][d + 1][r] *= ks ? al1 : al0;
                         }
                     }
-                    if constexpr (i + kPvLA < 8) fr[(i + kPvLA) % (kPvLA + 1)] = fetch(i + kPvLA);
+                    if constexpr (i + kPvLA < 8) fr[(i + kPvLA) % (kPvLA + 1)] = fetch(t, i + kPvLA);
                     __builtin_amdgcn_sched_barrier(0);
                 });
             };
+            prefetch(0);
+            barrier_lds();   // step 0
             for (int k = 1; k <= sg.n; ++k) {
                 const int t = k - 1, ts = t & 1;
                 const int l = lane_id64();
@@ -545,6 +558,7 @@ __global__ void __launch_bounds__(kT, 1) decode64_kernel(const DecodeArgs a) {
                 // the rescale is skipped when no head's max rose (alpha = 1 for all)
                 const bool rescale = __builtin_amdgcn_ballot_w64(al0 != 1.f || al1 != 1.f) != 0;
                 pv(t, al0, al1, rescale, P);
+                if (k < sg.n) prefetch(k);
                 barrier_lds();
             }
             barrier_lds();   // epilogue: fin_inv was written in step n - 1
