@@ -37,6 +37,15 @@
  *    workspace and the metadata buffer must be 16-byte aligned.
  *  - Entry points are thread-safe; calls that share a workspace or metadata
  *    buffer must be ordered by the caller (same stream or events).
+ *  - Debug mode: with the environment variable MLA_DEBUG set to "1", every
+ *    entry point that reads metadata, lengths, a block table or top-k indices
+ *    first synchronises ``stream``, copies those device arrays to the host and
+ *    runs the checks of mla_check_inputs on them (the scheduler also checks
+ *    the schedule it has just written; mla_combine checks that split_offsets
+ *    is a prefix sum from 0).  A failed check prints the first offending entry
+ *    to stderr and returns INVALID_ARG before anything is launched.  The mode
+ *    is for eager calls: on a stream that is capturing a graph it returns
+ *    INVALID_ARG.
  */
 #ifndef MLA_DECODE_H
 #define MLA_DECODE_H
@@ -48,7 +57,7 @@
 extern "C" {
 #endif
 
-#define MLA_DECODE_ABI_VERSION 3
+#define MLA_DECODE_ABI_VERSION 4
 
 typedef enum {
     MLA_OK = 0,
@@ -257,6 +266,33 @@ mla_status_t mla_debug_decode_partial(const mla_problem_t *problem, const void *
 mla_status_t mla_debug_gather_rows(const mla_problem_t *problem, const int32_t *table_or_indices,
                                    const int32_t *cache_seqlens, const int32_t *topk_length,
                                    int32_t *rows_out, void *stream);
+
+/* Host-side check of the arrays a decode call reads; every pointer is host
+ * memory (the MLA_DEBUG=1 mode runs it on copies of the device arrays).
+ *   meta_words       the metadata buffer's int32 words as written by
+ *                    mla_get_decode_metadata for ``meta`` (NULL: not checked).
+ *                    They must hold the schedule of the current lengths: every
+ *                    KV tile of every query token covered once, in order, with
+ *                    split counts, split offsets and first split slots that
+ *                    agree (reused metadata from other lengths fails here).
+ *   cache_seqlens    dense: [batch], each in [0, 64*max_blocks_per_seq]
+ *   table_or_indices dense: block_table, whose pages in use (the first
+ *                    ceil(cache_seqlens[b]/64) of row b) lie in [0, num_blocks);
+ *                    sparse: indices, whose entries before the token's top-k
+ *                    length are -1 or a row in [0, num_rows) (NULL: not checked)
+ *   topk_length      sparse: [batch*s_q] in [0, topk], or NULL
+ *   num_rows         rows the indices may name (0: num_blocks*64; s_kv for
+ *                    the prefill)
+ * The decode calls mask what this check rejects (see mla_sparse_decode_fwd)
+ * or clamp it (lengths); the check reports it as a caller error.  On a
+ * failure ``msg`` (if not NULL) receives a one-line description of the first
+ * offending entry.  Errors: INVALID_ARG (a check failed or a bad argument),
+ * UNSUPPORTED (the problem), METADATA_MISMATCH (``meta`` planned for another
+ * problem). */
+mla_status_t mla_check_inputs(const mla_problem_t *problem, const mla_metadata_t *meta,
+                              const int32_t *meta_words, const int32_t *cache_seqlens,
+                              const int32_t *table_or_indices, const int32_t *topk_length, int64_t num_rows,
+                              char *msg, size_t msg_len);
 
 #ifdef __cplusplus
 }

@@ -18,7 +18,7 @@ from ._lib import MlaError, Problem, Metadata  # noqa: F401
 
 __all__ = ["make_problem", "plan", "workspace_bytes", "get_decode_metadata", "decode_fwd",
            "sparse_decode_fwd", "sparse_prefill_fwd", "sparse_prefill", "combine", "debug_gather_rows", "Decoder",
-           "MlaError", "abi_version"]
+           "MlaError", "abi_version", "check_inputs"]
 
 
 def _ptr(t):
@@ -31,16 +31,65 @@ def _stream(stream):
     return ctypes.c_void_p(stream.cuda_stream)
 
 
-def _need(t, name, dtype, device=None):
+def _need(t, name, dtype, numel=None, last_dim=None):
+    """Check one tensor argument's dtype, contiguity, element count and last
+    dimension (where the problem fixes them).  Raises ValueError.  Placement is
+    checked afterwards, for all arguments at once, by ``_on_gpu``."""
     if t is None:
         raise ValueError(f"{name} is required")
-    if not t.is_cuda:
-        raise ValueError(f"{name} must be a device tensor")
     if dtype is not None and t.dtype != dtype:
         raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
+    if numel is not None and t.numel() != numel:
+        raise ValueError(f"{name} must have {numel} elements, got {t.numel()} (shape {tuple(t.shape)})")
+    if last_dim is not None and (t.dim() == 0 or t.shape[-1] != last_dim):
+        raise ValueError(f"{name} must have a last dimension of {last_dim}, got shape {tuple(t.shape)}")
     return t
+
+
+def _on_gpu(**tensors):
+    """Every given tensor (None: absent optional argument) lives on a GPU."""
+    for name, t in tensors.items():
+        if t is not None and t.device.type != "cuda":
+            raise ValueError(f"{name} must be a device tensor")
+
+
+# bytes of one cached token row per kv_format
+_RECORD_BYTES = {_lib.KV_BF16_576: 1152, _lib.KV_FP8_656: 656, _lib.KV_FP8_528: 528, _lib.KV_FP4_288: 288}
+
+
+def _out_dtype(problem):
+    return torch.float32 if problem.out_dtype == _lib.OUT_FP32 else torch.bfloat16
+
+
+def _check_q_out(problem, q, out, lse):
+    """q [batch, s_q, h_q, d_qk] bfloat16, out [batch, s_q, h_q, 512] in the problem's output dtype,
+    lse [batch, h_q, s_q] float32 (for prefill, batch = 1 and the leading dimension may be dropped)."""
+    B, S, H = problem.batch, problem.s_q, problem.h_q
+    _need(q, "q", torch.bfloat16, B * S * H * problem.d_qk, problem.d_qk)
+    _need(out, "out", _out_dtype(problem), B * S * H * 512, 512)
+    _need(lse, "lse", torch.float32, B * H * S)
+
+
+def _check_kv(problem, kv, rows, name="kv_cache"):
+    """At least ``rows`` cached rows in the problem's format: bfloat16 [..., 576] or uint8 [..., record bytes]."""
+    rec = _RECORD_BYTES[problem.kv_format]
+    if problem.kv_format == _lib.KV_BF16_576:
+        _need(kv, name, torch.bfloat16, None, 576)
+    else:
+        _need(kv, name, torch.uint8, None, rec)
+    if kv.numel() * kv.element_size() < rows * rec:
+        raise ValueError(f"{name} holds {kv.numel() * kv.element_size()} bytes, the problem needs {rows} rows of "
+                         f"{rec} bytes")
+
+
+def _check_table(problem, table_or_indices, cache_seqlens):
+    if problem.topk > 0:
+        _need(table_or_indices, "indices", torch.int32, problem.batch * problem.s_q * problem.topk)
+    else:
+        _need(table_or_indices, "block_table", torch.int32, problem.batch * problem.max_blocks_per_seq)
+        _need(cache_seqlens, "cache_seqlens", torch.int32, problem.batch)
 
 
 def abi_version():
@@ -76,10 +125,7 @@ def workspace_bytes(meta):
 def _optional(t, name, dtype, numel):
     if t is None:
         return None
-    _need(t, name, dtype)
-    if t.numel() != numel:
-        raise ValueError(f"{name} must have {numel} elements, got {t.numel()}")
-    return t
+    return _need(t, name, dtype, numel)
 
 
 def _topk_length(problem, topk_length):
@@ -102,9 +148,10 @@ def get_decode_metadata(problem, cache_seqlens, meta, meta_buf, stream=None, top
         raise ValueError("meta_buf too small")
     if problem.topk > 0:
         cache_seqlens = None
-    elif cache_seqlens is not None:
-        _need(cache_seqlens, "cache_seqlens", torch.int32)
+    else:
+        _need(cache_seqlens, "cache_seqlens", torch.int32, problem.batch)
     tl = _topk_length(problem, topk_length)
+    _on_gpu(meta_buf=meta_buf, cache_seqlens=cache_seqlens, topk_length=tl)
     meta.dev = meta_buf.data_ptr()
     _lib.check("mla_get_decode_metadata", lib.mla_get_decode_metadata(
         ctypes.byref(problem), _ptr(cache_seqlens), _ptr(tl), ctypes.byref(meta), _stream(stream)))
@@ -115,14 +162,13 @@ def decode_fwd(problem, q, kv_cache, block_table, cache_seqlens, meta, workspace
                attn_sink=None):
     """Dense paged decode (mla_decode_fwd)."""
     lib = _lib.load()
-    _need(q, "q", torch.bfloat16)
-    _need(kv_cache, "kv_cache", None)
-    _need(block_table, "block_table", torch.int32)
-    _need(cache_seqlens, "cache_seqlens", torch.int32)
+    _check_q_out(problem, q, out, lse)
+    _check_kv(problem, kv_cache, problem.num_blocks * 64)
+    _check_table(problem, block_table, cache_seqlens)
     _need(workspace, "workspace", None)
-    _need(out, "out", None)
-    _need(lse, "lse", torch.float32)
     sink = _attn_sink(problem.h_q, attn_sink)
+    _on_gpu(q=q, kv_cache=kv_cache, block_table=block_table, cache_seqlens=cache_seqlens, workspace=workspace,
+            out=out, lse=lse, attn_sink=sink)
     _lib.check("mla_decode_fwd", lib.mla_decode_fwd(
         ctypes.byref(problem), _ptr(q), _ptr(kv_cache), _ptr(block_table), _ptr(cache_seqlens), _ptr(sink),
         ctypes.byref(meta), _ptr(workspace), workspace.numel() * workspace.element_size(), _ptr(out), _ptr(lse),
@@ -133,13 +179,13 @@ def sparse_decode_fwd(problem, q, kv_cache, indices, meta, workspace, out, lse, 
                       attn_sink=None):
     """Top-k sparse decode (mla_sparse_decode_fwd)."""
     lib = _lib.load()
-    _need(q, "q", torch.bfloat16)
-    _need(kv_cache, "kv_cache", None)
-    _need(indices, "indices", torch.int32)
+    _check_q_out(problem, q, out, lse)
+    _check_kv(problem, kv_cache, problem.num_blocks * 64)
+    _check_table(problem, indices, None)
     _need(workspace, "workspace", None)
-    _need(out, "out", None)
-    _need(lse, "lse", torch.float32)
     tl, sink = _topk_length(problem, topk_length), _attn_sink(problem.h_q, attn_sink)
+    _on_gpu(q=q, kv_cache=kv_cache, indices=indices, workspace=workspace, out=out, lse=lse, topk_length=tl,
+            attn_sink=sink)
     _lib.check("mla_sparse_decode_fwd", lib.mla_sparse_decode_fwd(
         ctypes.byref(problem), _ptr(q), _ptr(kv_cache), _ptr(indices), _ptr(tl), _ptr(sink), ctypes.byref(meta),
         _ptr(workspace),
@@ -150,13 +196,12 @@ def sparse_prefill_fwd(problem, s_kv, q, kv, indices, meta, workspace, out, lse,
                        attn_sink=None):
     """Top-k sparse prefill over a flat cache of s_kv rows (mla_sparse_prefill_fwd); ``problem`` has batch 1."""
     lib = _lib.load()
-    _need(q, "q", torch.bfloat16)
-    _need(kv, "kv", None)
-    _need(indices, "indices", torch.int32)
+    _check_q_out(problem, q, out, lse)
+    _check_kv(problem, kv, int(s_kv), "kv")
+    _check_table(problem, indices, None)
     _need(workspace, "workspace", None)
-    _need(out, "out", None)
-    _need(lse, "lse", torch.float32)
     tl, sink = _topk_length(problem, topk_length), _attn_sink(problem.h_q, attn_sink)
+    _on_gpu(q=q, kv=kv, indices=indices, workspace=workspace, out=out, lse=lse, topk_length=tl, attn_sink=sink)
     _lib.check("mla_sparse_prefill_fwd", lib.mla_sparse_prefill_fwd(
         ctypes.byref(problem), int(s_kv), _ptr(q), _ptr(kv), _ptr(indices), _ptr(tl), _ptr(sink),
         ctypes.byref(meta), _ptr(workspace), workspace.numel() * workspace.element_size(), _ptr(out), _ptr(lse),
@@ -170,7 +215,13 @@ def sparse_prefill(q, kv, indices, sm_scale=None, topk_length=None, attn_sink=No
     schedules and allocates the outputs and workspace with torch on q's device, then runs the library."""
     s_q, h_q = int(q.shape[0]), int(q.shape[1])
     s_kv, topk = int(kv.shape[0]), int(indices.shape[-1])
-    fmt = "bf16" if kv.dtype != torch.uint8 else {528: "fp8_528", 288: "fp4_288"}.get(int(kv.shape[-1]), "fp8")
+    if kv.dtype == torch.bfloat16:
+        fmt = "bf16"
+    elif kv.dtype == torch.uint8 and int(kv.shape[-1]) in (656, 528, 288):
+        fmt = {656: "fp8", 528: "fp8_528", 288: "fp4_288"}[int(kv.shape[-1])]
+    else:
+        raise ValueError(f"kv must be bfloat16 [s_kv, 1, 576] or uint8 records of 656, 528 or 288 bytes, got "
+                         f"{kv.dtype} {tuple(kv.shape)}")
     p = make_problem(1, s_q, h_q, (s_kv + 63) // 64, topk=topk, kv_format=fmt, out_dtype=out_dtype,
                      softmax_scale=sm_scale, rescale_threshold=rescale_threshold)
     m = plan(p, num_cus)
@@ -187,13 +238,19 @@ def sparse_prefill(q, kv, indices, sm_scale=None, topk_length=None, attn_sink=No
 def combine(num_items, h_q, s_q, o_part, lse_part, split_offsets, out, lse, stream=None, attn_sink=None):
     """Standalone LSE merge of split partials (mla_combine)."""
     lib = _lib.load()
-    _need(o_part, "o_part", torch.float32)
+    n, H = int(num_items), int(h_q)
+    if out is None or out.dtype not in (torch.bfloat16, torch.float32):
+        raise ValueError("out must be a bfloat16 or float32 tensor")
     _need(lse_part, "lse_part", torch.float32)
-    _need(split_offsets, "split_offsets", torch.int32)
-    _need(out, "out", None)
-    _need(lse, "lse", torch.float32)
+    _need(o_part, "o_part", torch.float32, lse_part.numel() * 512)
+    if lse_part.numel() % max(H, 1):
+        raise ValueError(f"lse_part must hold whole [h_q] rows, got {lse_part.numel()} elements")
+    _need(split_offsets, "split_offsets", torch.int32, n + 1)
+    _need(out, "out", out.dtype, n * H * 512, 512)
+    _need(lse, "lse", torch.float32, n * H)
     od = {torch.bfloat16: _lib.OUT_BF16, torch.float32: _lib.OUT_FP32}[out.dtype]
     sink = _attn_sink(int(h_q), attn_sink)
+    _on_gpu(o_part=o_part, lse_part=lse_part, split_offsets=split_offsets, out=out, lse=lse, attn_sink=sink)
     _lib.check("mla_combine", lib.mla_combine(int(num_items), int(h_q), int(s_q), _ptr(o_part), _ptr(lse_part),
                                               _ptr(split_offsets), _ptr(sink), od, _ptr(out), _ptr(lse),
                                               _stream(stream)))
@@ -201,9 +258,12 @@ def combine(num_items, h_q, s_q, o_part, lse_part, split_offsets, out, lse, stre
 
 def debug_gather_rows(problem, table_or_indices, cache_seqlens, rows_out, stream=None, topk_length=None):
     lib = _lib.load()
-    _need(table_or_indices, "table_or_indices", torch.int32)
-    _need(rows_out, "rows_out", torch.int32)
+    _check_table(problem, table_or_indices, cache_seqlens)
+    stride = 64 * ((problem.topk + 63) // 64) if problem.topk > 0 else 64 * problem.max_blocks_per_seq
+    _need(rows_out, "rows_out", torch.int32, problem.batch * problem.s_q * stride)
     tl = _topk_length(problem, topk_length)
+    _on_gpu(table_or_indices=table_or_indices, cache_seqlens=None if problem.topk > 0 else cache_seqlens,
+            rows_out=rows_out, topk_length=tl)
     _lib.check("mla_debug_gather_rows", lib.mla_debug_gather_rows(
         ctypes.byref(problem), _ptr(table_or_indices), _ptr(cache_seqlens), _ptr(tl), _ptr(rows_out),
         _stream(stream)))
@@ -214,17 +274,44 @@ def debug_decode_partial(problem, q, kv_cache, table_or_indices, cache_seqlens, 
     """Test hook: the partial-attention kernel alone (mla_debug_decode_partial).  ``production``: split
     partials in the decode call's own format (the launch a decode step makes) instead of mla_combine's."""
     lib = _lib.load()
-    _need(q, "q", torch.bfloat16)
-    _need(kv_cache, "kv_cache", None)
-    _need(table_or_indices, "table_or_indices", torch.int32)
+    _check_q_out(problem, q, out, lse)
+    _check_kv(problem, kv_cache, problem.num_blocks * 64)
+    _check_table(problem, table_or_indices, cache_seqlens)
     _need(workspace, "workspace", None)
-    _need(out, "out", None)
-    _need(lse, "lse", torch.float32)
     tl, sink = _topk_length(problem, topk_length), _attn_sink(problem.h_q, attn_sink)
+    _on_gpu(q=q, kv_cache=kv_cache, table_or_indices=table_or_indices,
+            cache_seqlens=None if problem.topk > 0 else cache_seqlens, workspace=workspace, out=out, lse=lse,
+            topk_length=tl, attn_sink=sink)
     _lib.check("mla_debug_decode_partial", lib.mla_debug_decode_partial(
         ctypes.byref(problem), _ptr(q), _ptr(kv_cache), _ptr(table_or_indices), _ptr(cache_seqlens), _ptr(tl),
         _ptr(sink), ctypes.byref(meta), _ptr(workspace), workspace.numel() * workspace.element_size(), _ptr(out), _ptr(lse),
         1 if production else 0, _stream(stream)))
+
+
+def check_inputs(problem, meta=None, meta_words=None, cache_seqlens=None, table_or_indices=None, topk_length=None,
+                 num_rows=0):
+    """Host-side check of a decode call's arrays (mla_check_inputs): numpy or CPU-tensor int32 arrays, each
+    optional as in the C call.  Returns None when they pass; raises MlaError with the first offending entry."""
+    import numpy as np
+    lib = _lib.load()
+    keep = []
+
+    def host(a, name):
+        if a is None:
+            return None
+        a = np.ascontiguousarray(a.cpu().numpy() if isinstance(a, torch.Tensor) else a)
+        if a.dtype != np.int32:
+            raise ValueError(f"{name} must be int32, got {a.dtype}")
+        keep.append(a)
+        return ctypes.c_void_p(a.ctypes.data)
+
+    msg = ctypes.create_string_buffer(256)
+    st = lib.mla_check_inputs(ctypes.byref(problem), ctypes.byref(meta) if meta is not None else None,
+                              host(meta_words, "meta_words"), host(cache_seqlens, "cache_seqlens"),
+                              host(table_or_indices, "table_or_indices"), host(topk_length, "topk_length"),
+                              int(num_rows), msg, len(msg))
+    if st != _lib.MLA_OK:
+        raise MlaError("mla_check_inputs", st, msg.value.decode() or lib.mla_status_string(st).decode())
 
 
 class Decoder:

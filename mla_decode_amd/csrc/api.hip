@@ -7,6 +7,7 @@
 #include <mutex>
 
 #include "../../include/mla_decode.h"
+#include "check.h"
 #include "common.h"
 #include "kernels.h"
 
@@ -121,6 +122,13 @@ mla_status_t run_decode(const mla_problem_t* p, bool sparse, const void* q, cons
     if (!ws || !aligned16(ws)) return need == 0 ? MLA_ERR_INVALID_ARG : MLA_ERR_WORKSPACE_TOO_SMALL;
     if (ws_bytes < need) return MLA_ERR_WORKSPACE_TOO_SMALL;
 
+    hipStream_t s = (hipStream_t)stream;
+    if (mla::debug_enabled()) {
+        st = mla::debug_check_call(p, meta, true, cache_seqlens, sparse ? indices : block_table, topk_length,
+                                   num_rows, s, sparse ? "sparse decode" : "mla_decode_fwd");
+        if (st != MLA_OK) return st;
+    }
+
     const int64_t slots = meta->max_splits;
     mla::DecodeArgs a{};
     a.q = q;
@@ -154,7 +162,6 @@ mla_status_t run_decode(const mla_problem_t* p, bool sparse, const void* q, cons
     a.max_slots = (int)slots;
     a.scale_log2 = p->softmax_scale * 1.4426950408889634f;
     a.rescale_tau = p->rescale_threshold;
-    hipStream_t s = (hipStream_t)stream;
     const hipError_t e = uses_decode64(p) ? mla::launch_decode64(a, s) : mla::launch_decode(a, sparse, p->kv_format, s);
     if (e != hipSuccess) return MLA_ERR_HIP;
 
@@ -229,6 +236,13 @@ mla_status_t mla_get_decode_metadata(const mla_problem_t* problem, const int32_t
     st = check_meta(problem, meta);
     if (st != MLA_OK) return st;
     if (problem->topk == 0 && !cache_seqlens) return MLA_ERR_INVALID_ARG;
+    const bool debug = mla::debug_enabled();
+    hipStream_t s = (hipStream_t)stream;
+    if (debug) {
+        st = mla::debug_check_call(problem, meta, false, cache_seqlens, nullptr, topk_length, 0, s,
+                                   "mla_get_decode_metadata");
+        if (st != MLA_OK) return st;
+    }
     mla::MetaArgs a{};
     a.cache_seqlens = problem->topk > 0 ? topk_length : cache_seqlens;
     a.meta = (int32_t*)meta->dev;
@@ -239,7 +253,11 @@ mla_status_t mla_get_decode_metadata(const mla_problem_t* problem, const int32_t
     a.causal = problem->causal;
     a.num_parts = meta->num_partitions;
     a.fixed_overhead = meta->fixed_overhead;
-    return mla::launch_metadata(a, (hipStream_t)stream) == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+    if (mla::launch_metadata(a, s) != hipSuccess) return MLA_ERR_HIP;
+    // debug mode: the schedule just written is checked as well
+    return debug ? mla::debug_check_call(problem, meta, true, cache_seqlens, nullptr, topk_length, 0, s,
+                                         "mla_get_decode_metadata")
+                 : MLA_OK;
 }
 
 mla_status_t mla_decode_fwd(const mla_problem_t* problem, const void* q, const void* kv_cache,
@@ -276,6 +294,10 @@ mla_status_t mla_combine(int32_t num_items, int32_t h_q, int32_t s_q, const floa
     if (!aligned16(o_part) || !aligned16(out)) return MLA_ERR_INVALID_ARG;
     if (out_dtype != MLA_OUT_BF16 && out_dtype != MLA_OUT_FP32) return MLA_ERR_INVALID_ARG;
     if ((int64_t)num_items * h_q >= ((int64_t)1 << 31) / 4) return MLA_ERR_UNSUPPORTED;
+    if (mla::debug_enabled()) {
+        const mla_status_t st = mla::debug_check_offsets(split_offsets, num_items, (hipStream_t)stream);
+        if (st != MLA_OK) return st;
+    }
     mla::CombineArgs c{};
     c.o_part = o_part;
     c.lse_part = lse_part;
@@ -309,6 +331,11 @@ mla_status_t mla_debug_gather_rows(const mla_problem_t* problem, const int32_t* 
     mla_status_t st = validate(problem);
     if (st != MLA_OK) return st;
     if (!table_or_indices || !rows_out || (problem->topk == 0 && !cache_seqlens)) return MLA_ERR_INVALID_ARG;
+    if (mla::debug_enabled()) {
+        st = mla::debug_check_call(problem, nullptr, false, cache_seqlens, table_or_indices, topk_length, 0,
+                                   (hipStream_t)stream, "mla_debug_gather_rows");
+        if (st != MLA_OK) return st;
+    }
     mla::GatherArgs g{};
     g.table_or_indices = table_or_indices;
     g.cache_seqlens = problem->topk > 0 ? topk_length : cache_seqlens;
@@ -321,6 +348,24 @@ mla_status_t mla_debug_gather_rows(const mla_problem_t* problem, const int32_t* 
     g.causal = problem->causal;
     g.row_stride = problem->topk > 0 ? 64 * ((problem->topk + 63) / 64) : 64 * problem->max_blocks_per_seq;
     return mla::launch_gather(g, (hipStream_t)stream) == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+}
+
+mla_status_t mla_check_inputs(const mla_problem_t* problem, const mla_metadata_t* meta, const int32_t* meta_words,
+                              const int32_t* cache_seqlens, const int32_t* table_or_indices,
+                              const int32_t* topk_length, int64_t num_rows, char* msg, size_t msg_len) {
+    if (msg && msg_len) msg[0] = 0;
+    mla_status_t st = validate(problem);
+    if (st != MLA_OK) return st;
+    if (meta_words) {
+        if (!meta) return MLA_ERR_INVALID_ARG;
+        if (!same_problem(meta->sig, *problem) || meta->num_partitions < 1 ||
+            meta->num_head_blocks != (problem->h_q + heads_per_block(problem) - 1) / heads_per_block(problem) ||
+            meta->max_splits != (int64_t)problem->batch * problem->s_q + meta->num_partitions)
+            return MLA_ERR_METADATA_MISMATCH;
+    }
+    if (num_rows < 0 || num_rows > (int64_t)problem->num_blocks * kBlock) return MLA_ERR_INVALID_ARG;
+    return mla::check_host_arrays(problem, meta, meta_words, cache_seqlens, table_or_indices, topk_length, num_rows,
+                                  msg, msg_len);
 }
 
 }  // extern "C"

@@ -51,14 +51,14 @@ __device__ __forceinline__ T sload(const T* p) {
     return *(const __attribute__((address_space(4))) T*)(p);
 }
 
-__device__ __forceinline__ int visible_len(int L, int s_q, int i, int causal) {
+__host__ __device__ __forceinline__ int visible_len(int L, int s_q, int i, int causal) {
     if (!causal) return L;
     int v = L - s_q + 1 + i;
     return v < 0 ? 0 : (v > L ? L : v);
 }
 
 // Clamp a cache length read from device memory to what the block table holds.
-__device__ __forceinline__ int clamp_len(int L, int max_blocks) {
+__host__ __device__ __forceinline__ int clamp_len(int L, int max_blocks) {
     int cap = max_blocks * kBlock;
     return L < 0 ? 0 : (L > cap ? cap : L);
 }
@@ -79,7 +79,7 @@ __device__ __forceinline__ int64_t sparse_entry_row(int64_t r, int64_t num_rows)
 
 // Top-k slots item j attends to: its first topk_length[j] entries (clamped to
 // [0, topk]), or all topk without a length array.
-__device__ __forceinline__ int topk_slots(int len, int topk) {
+__host__ __device__ __forceinline__ int topk_slots(int len, int topk) {
     return len < 0 ? 0 : (len > topk ? topk : len);
 }
 

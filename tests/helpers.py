@@ -65,8 +65,13 @@ def oracle(w, items=None, kv=None):
                     items=items, attn_sink=sink)
 
 
-def compare(got_out, got_lse, ref_out, ref_lse, items=None, rel_l2=OUT_REL_L2, max_abs=OUT_MAX_ABS, lse_abs=LSE_ABS):
-    """Element-wise comparison on the selected items (default all); returns stats."""
+def compare(got_out, got_lse, ref_out, ref_lse, items=None, rel_l2=OUT_REL_L2, max_abs=OUT_MAX_ABS, lse_abs=LSE_ABS,
+            max_abs_rel=MAX_ABS_REL):
+    """Element-wise comparison on the selected items (default all); returns stats.
+
+    Every element satisfies |got - ref| <= max_abs + max_abs_rel * |ref|;
+    ``max_abs_rel=0`` makes it the literal max-abs bound (the full-size
+    workloads, whose outputs stay below 2 in magnitude, use that)."""
     B, S = ref_out.shape[:2]
     if items is None:
         items = [(b, i) for b in range(B) for i in range(S)]
@@ -78,7 +83,7 @@ def compare(got_out, got_lse, ref_out, ref_lse, items=None, rel_l2=OUT_REL_L2, m
     nrm = np.linalg.norm(ro)
     rel = np.linalg.norm(go - ro) / nrm if nrm > 0 else np.linalg.norm(go)
     mab = float(np.max(np.abs(go - ro))) if go.size else 0.0
-    excess = float(np.max(np.abs(go - ro) - MAX_ABS_REL * np.abs(ro))) if go.size else 0.0
+    excess = float(np.max(np.abs(go - ro) - max_abs_rel * np.abs(ro))) if go.size else 0.0
     fin = np.isfinite(rl)
     assert np.array_equal(np.isneginf(gl), np.isneginf(rl)), "-inf lse positions differ"
     lerr = float(np.max(np.abs(gl[fin] - rl[fin]))) if fin.any() else 0.0

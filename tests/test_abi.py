@@ -35,7 +35,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_abi_version_and_status_strings(lib):
-    assert lib.mla_abi_version() == 3
+    assert lib.mla_abi_version() == 4
     for s in range(6):
         assert lib.mla_status_string(s)
     assert lib.mla_status_string(99) == b"unknown status"

@@ -35,6 +35,6 @@ def test_fp8_sparse_headline_sampled(topk, items):
     go, gl, dec = run_library(w)
     print(f"partitions {dec.meta.num_partitions}, split slots {dec.meta.max_splits}", flush=True)
     ro, rl = oracle(w, items=items, kv=kv_host_rows(w, items))
-    print(compare(go, gl, ro, rl, items=items, rel_l2=FP8_REL_L2, max_abs=5e-2), flush=True)
+    print(compare(go, gl, ro, rl, items=items, rel_l2=FP8_REL_L2, max_abs=1e-2), flush=True)
     # every query token produced finite output and lse
     assert np.all(np.isfinite(go)) and np.all(np.isfinite(gl))

@@ -2,8 +2,8 @@
 
 Sizes: small cases span several 64-token tiles, ragged tails and several
 splits so the oracle checks every output; the five full-size workloads are
-checked on sampled query tokens (every head, every dim of each sampled token)
-in the launch configuration the benchmark times.
+checked whole (every output element and lse) in the launch configuration the
+benchmark times.
 """
 
 import numpy as np
@@ -166,7 +166,7 @@ def test_long_partition_crosses_page_window(kv_format):
         if kv_format == "bf16":
             _say(compare(go, gl, ro, rl))
         else:
-            _say(compare(go, gl, ro, rl, rel_l2=FP8_REL_L2, max_abs=5e-2))
+            _say(compare(go, gl, ro, rl, rel_l2=FP8_REL_L2, max_abs=1e-2))
 
 
 def test_block_table_reshuffle_is_bitwise_invariant():
@@ -215,7 +215,7 @@ def test_fp8_small():
     w = make_fp8_dense(3, 1, 128, [70, 300, 1], seed=7, device=DEV)
     go, gl, _ = run_library(w)
     ro, rl = oracle(w)
-    _say(compare(go, gl, ro, rl, rel_l2=FP8_REL_L2, max_abs=5e-2))
+    _say(compare(go, gl, ro, rl, rel_l2=FP8_REL_L2, max_abs=1e-2))
 
 
 def test_fp8_sparse_small():
@@ -224,7 +224,7 @@ def test_fp8_sparse_small():
                     kv_format='fp8')
     go, gl, _ = run_library(w)
     ro, rl = oracle(w)
-    _say(compare(go, gl, ro, rl, rel_l2=FP8_REL_L2, max_abs=5e-2))
+    _say(compare(go, gl, ro, rl, rel_l2=FP8_REL_L2, max_abs=1e-2))
 
 
 # ------------------------------------------------------------------ combine entry point
@@ -318,28 +318,30 @@ def test_partial_hook_plus_combine_equals_decode(out_dtype):
             _say(f"bf16 outputs differing: {float((a != b).float().mean()):.4f}")
 
 
-# ------------------------------------------------------------------ full-size workloads (sampled)
+# ------------------------------------------------------------------ full-size workloads (whole tensors)
 
-def _sampled(w, items):
-    go, gl, _ = run_library(w)
-    ro, rl = oracle(w, items=items)
-    return compare(go, gl, ro, rl, items=items)
+def _whole(w, **kw):
+    """Every output element and lse of a full-size workload against the
+    oracle, with the literal max-abs bound (no magnitude-relative slack)."""
+    go, gl, dec = run_library(w)
+    ro, rl = oracle(w)
+    stats = compare(go, gl, ro, rl, max_abs_rel=0.0, **kw)
+    assert float(np.max(np.abs(go - ro))) <= kw.get("max_abs", 1e-2)
+    assert np.all(np.isfinite(gl))
+    return stats
 
 
-def test_config2_sampled():
-    _say("config2")
-    w = make_config(2, device=DEV)
-    _say(_sampled(w, [(b, 0) for b in (0, 1, 17, 31, 32, 50, 62, 63)]))
+def test_config2_whole():
+    _say("config2 b=64 s_q=1 h_q=128 seqlen=4096 bf16")
+    _say(_whole(make_config(2, device=DEV)))
 
 
-def test_config3_sampled():
-    _say("config3")
+def test_config3_whole():
+    _say("config3 b=128 s_q=2 causal h_q=128 seqlen U[1,8192] bf16")
     w = make_config(3, device=DEV)
     lens = w.cache_seqlens.cpu().numpy()
-    order = np.argsort(lens)
-    bs = sorted(set([int(order[0]), int(order[1]), int(order[-1]), int(order[len(order) // 2]), 0, 77, 127]))
-    _say("lens", [int(lens[b]) for b in bs])
-    _say(_sampled(w, [(b, i) for b in bs for i in range(2)]))
+    _say("lens min/median/max", int(lens.min()), int(np.median(lens)), int(lens.max()))
+    _say(_whole(w))
 
 
 def test_config4_full():
@@ -347,16 +349,12 @@ def test_config4_full():
     w = make_config(4, device=DEV)
     go, gl, _ = run_library(w)
     ro, rl = oracle(w)
-    _say(compare(go, gl, ro, rl))
+    _say(compare(go, gl, ro, rl, max_abs_rel=0.0))
 
 
-def test_config5_sampled():
-    _say("config5")
-    w = make_config(5, device=DEV)
-    items = [(b, 0) for b in (0, 9, 31)]
-    go, gl, _ = run_library(w)
-    ro, rl = oracle(w, items=items)
-    _say(compare(go, gl, ro, rl, items=items, rel_l2=FP8_REL_L2, max_abs=5e-2))
+def test_config5_whole():
+    _say("config5 b=32 s_q=1 h_q=128 seqlen=16384 fp8 cache")
+    _say(_whole(make_config(5, device=DEV), rel_l2=FP8_REL_L2, max_abs=1e-2))
 
 
 # ------------------------------------------------------------------ peaked rows: top-k order invariance
