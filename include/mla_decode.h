@@ -57,7 +57,7 @@
 extern "C" {
 #endif
 
-#define MLA_DECODE_ABI_VERSION 4
+#define MLA_DECODE_ABI_VERSION 5
 
 typedef enum {
     MLA_OK = 0,
@@ -266,6 +266,31 @@ mla_status_t mla_debug_decode_partial(const mla_problem_t *problem, const void *
 mla_status_t mla_debug_gather_rows(const mla_problem_t *problem, const int32_t *table_or_indices,
                                    const int32_t *cache_seqlens, const int32_t *topk_length,
                                    int32_t *rows_out, void *stream);
+
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): one whole
+ * decode step -- mla_plan with ``num_cus`` (0: the device's compute units),
+ * the scheduler of mla_get_decode_metadata, then mla_decode_fwd (dense,
+ * problem->topk == 0: table_or_indices = block_table, cache_seqlens
+ * required) or mla_sparse_decode_fwd (table_or_indices = indices,
+ * topk_length optional) -- with the metadata and the split partials in a
+ * scratch area the library holds in device memory (128 MiB per device,
+ * reserved when the library is loaded on that device and kept until the
+ * process ends) instead of a metadata buffer and a workspace.  The caller
+ * passes inputs and outputs as for those calls; the call allocates nothing
+ * and makes the same kernel launches as that sequence, so its outputs equal
+ * theirs bit for bit.  Every call on a device shares that device's scratch:
+ * calls that may overlap on one device (different streams, threads or
+ * processes without ordering) race and must be serialised by the caller.
+ * Errors: those of mla_plan, mla_get_decode_metadata and the decode call;
+ * WORKSPACE_TOO_SMALL, before anything touches the device, when the plan
+ * needs more than 64 KiB of metadata or more than 128 MiB - 64 KiB of
+ * partials (mla_workspace_bytes), e.g. more than about 500 split slots of
+ * 128 heads. */
+mla_status_t mla_decode_step_noalloc(const mla_problem_t *problem, int32_t num_cus, const void *q,
+                                     const void *kv_cache, const int32_t *table_or_indices,
+                                     const int32_t *cache_seqlens, const int32_t *topk_length,
+                                     const float *attn_sink, void *out, float *lse, void *stream);
 
 /* Host-side check of the arrays a decode call reads; every pointer is host
  * memory (the MLA_DEBUG=1 mode runs it on copies of the device arrays).

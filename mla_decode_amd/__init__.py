@@ -18,7 +18,7 @@ from ._lib import MlaError, Problem, Metadata  # noqa: F401
 
 __all__ = ["make_problem", "plan", "workspace_bytes", "get_decode_metadata", "decode_fwd",
            "sparse_decode_fwd", "sparse_prefill_fwd", "sparse_prefill", "combine", "debug_gather_rows", "Decoder",
-           "MlaError", "abi_version", "check_inputs"]
+           "MlaError", "abi_version", "check_inputs", "decode_step_noalloc"]
 
 
 def _ptr(t):
@@ -286,6 +286,23 @@ def debug_decode_partial(problem, q, kv_cache, table_or_indices, cache_seqlens, 
         ctypes.byref(problem), _ptr(q), _ptr(kv_cache), _ptr(table_or_indices), _ptr(cache_seqlens), _ptr(tl),
         _ptr(sink), ctypes.byref(meta), _ptr(workspace), workspace.numel() * workspace.element_size(), _ptr(out), _ptr(lse),
         1 if production else 0, _stream(stream)))
+
+
+def decode_step_noalloc(problem, q, kv_cache, table_or_indices, out, lse, cache_seqlens=None, topk_length=None,
+                        attn_sink=None, num_cus=0, stream=None):
+    """A whole decode step (plan, scheduler, decode, combine) in the library's own device scratch
+    (mla_decode_step_noalloc): no metadata buffer or workspace; calls that overlap on one device race."""
+    lib = _lib.load()
+    _check_q_out(problem, q, out, lse)
+    _check_kv(problem, kv_cache, problem.num_blocks * 64)
+    _check_table(problem, table_or_indices, cache_seqlens)
+    tl, sink = _topk_length(problem, topk_length), _attn_sink(problem.h_q, attn_sink)
+    dense_len = None if problem.topk > 0 else cache_seqlens
+    _on_gpu(q=q, kv_cache=kv_cache, table_or_indices=table_or_indices, cache_seqlens=dense_len, out=out, lse=lse,
+            topk_length=tl, attn_sink=sink)
+    _lib.check("mla_decode_step_noalloc", lib.mla_decode_step_noalloc(
+        ctypes.byref(problem), int(num_cus), _ptr(q), _ptr(kv_cache), _ptr(table_or_indices), _ptr(dense_len),
+        _ptr(tl), _ptr(sink), _ptr(out), _ptr(lse), _stream(stream)))
 
 
 def check_inputs(problem, meta=None, meta_words=None, cache_seqlens=None, table_or_indices=None, topk_length=None,

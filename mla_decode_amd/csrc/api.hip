@@ -21,6 +21,31 @@ constexpr int kMaxDevices = 64;
 int g_cu_count[kMaxDevices];
 std::mutex g_cu_mu;
 
+// Scratch memory of mla_decode_step_noalloc: the schedule's metadata words,
+// then the split partials.  Each device holds its own copy for the life of
+// the process.  Host code never names the array itself (on the host it is
+// only a stand-in for the symbol): it uses the device address that
+// hipGetSymbolAddress returns for the current device.
+constexpr size_t kScratchBytes = size_t(128) << 20;
+constexpr size_t kScratchMetaBytes = size_t(64) << 10;   // metadata words, at the start
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+void* g_scratch_ptr[kMaxDevices];
+std::mutex g_scratch_mu;
+
+mla_status_t device_scratch(void** out) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return MLA_ERR_HIP;
+    std::lock_guard<std::mutex> g(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* ptr = nullptr;
+        if (hipGetSymbolAddress((void**)&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return MLA_ERR_HIP;
+        g_scratch_ptr[dev] = ptr;
+    }
+    *out = g_scratch_ptr[dev];
+    return MLA_OK;
+}
+
 mla_status_t device_cus(int32_t* out) {
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return MLA_ERR_HIP;
@@ -348,6 +373,31 @@ mla_status_t mla_debug_gather_rows(const mla_problem_t* problem, const int32_t* 
     g.causal = problem->causal;
     g.row_stride = problem->topk > 0 ? 64 * ((problem->topk + 63) / 64) : 64 * problem->max_blocks_per_seq;
     return mla::launch_gather(g, (hipStream_t)stream) == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+}
+
+mla_status_t mla_decode_step_noalloc(const mla_problem_t* problem, int32_t num_cus, const void* q,
+                                     const void* kv_cache, const int32_t* table_or_indices,
+                                     const int32_t* cache_seqlens, const int32_t* topk_length,
+                                     const float* attn_sink, void* out, float* lse, void* stream) {
+    mla_metadata_t m{};
+    mla_status_t st = mla_plan(problem, num_cus, &m);
+    if (st != MLA_OK) return st;
+    // sizes are checked before the device is touched
+    if (m.bytes > kScratchMetaBytes || mla_workspace_bytes(&m) > kScratchBytes - kScratchMetaBytes)
+        return MLA_ERR_WORKSPACE_TOO_SMALL;
+    const bool sparse = problem->topk > 0;
+    if (!table_or_indices || (!sparse && !cache_seqlens)) return MLA_ERR_INVALID_ARG;
+    void* base = nullptr;
+    st = device_scratch(&base);
+    if (st != MLA_OK) return st;
+    m.dev = base;
+    st = mla_get_decode_metadata(problem, sparse ? nullptr : cache_seqlens, sparse ? topk_length : nullptr, &m,
+                                 stream);
+    if (st != MLA_OK) return st;
+    return run_decode(problem, sparse, q, kv_cache, sparse ? nullptr : table_or_indices,
+                      sparse ? nullptr : cache_seqlens, sparse ? table_or_indices : nullptr,
+                      sparse ? topk_length : nullptr, attn_sink, &m, (unsigned char*)base + kScratchMetaBytes,
+                      kScratchBytes - kScratchMetaBytes, out, lse, stream);
 }
 
 mla_status_t mla_check_inputs(const mla_problem_t* problem, const mla_metadata_t* meta, const int32_t* meta_words,

@@ -35,7 +35,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_abi_version_and_status_strings(lib):
-    assert lib.mla_abi_version() == 4
+    assert lib.mla_abi_version() == 5
     for s in range(6):
         assert lib.mla_status_string(s)
     assert lib.mla_status_string(99) == b"unknown status"
@@ -165,3 +165,14 @@ def test_512_wide_records_need_the_512_wide_head_and_top_k(fmt):
     with pytest.raises(mla.MlaError) as e:
         mla.plan(p, num_cus=256)
     assert e.value.status == 2
+
+
+def test_noalloc_step_rejects_oversized_plans_before_touching_the_device(lib):
+    import mla_decode_amd as mla
+    fake = ctypes.c_void_p(1 << 20)       # never dereferenced: the size check fails first
+    p = _problem(batch=2048, num_blocks=4096, max_blocks_per_seq=64)   # 2176 split slots of 128 heads
+    assert lib.mla_decode_step_noalloc(ctypes.byref(p), 256, fake, fake, fake, fake, None, None, fake, fake,
+                                       None) == 3
+    p = _problem(batch=0)
+    assert lib.mla_decode_step_noalloc(ctypes.byref(p), 256, fake, fake, fake, fake, None, None, fake, fake,
+                                       None) == 1
