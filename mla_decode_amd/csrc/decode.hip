@@ -1,4 +1,7 @@
-// Split-KV partial-attention kernel for absorbed-MLA decode on gfx950.
+// Split-KV partial-attention kernel for absorbed-MLA decode on gfx950: the
+// top-k (sparse) calls and the quantised caches (656-, 528- and 288-byte
+// records).  Dense decode over a bf16 cache runs the 64-heads-per-workgroup
+// kernel of decode64.hip instead.
 //
 // One workgroup = 128 query heads x one scheduler partition (a contiguous run
 // of 64-token KV pages, possibly spanning several items), so every cache page

@@ -129,6 +129,12 @@ __device__ __forceinline__ void prefetch_x1(const i32x4& rs, int voff, int lds) 
                      :: "s"(lds), "v"(voff), "s"(rs) : "memory", "m0");
 }
 
+__device__ __forceinline__ void barrier_only() {
+    __asm__ volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    __asm__ volatile("" ::: "memory");
+}
+
 __device__ __forceinline__ void barrier_lds() {
     __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0); vmcnt, expcnt untouched
     __asm__ volatile("" ::: "memory");
@@ -328,7 +334,10 @@ __global__ void __launch_bounds__(kT, 1) decode64_kernel(const DecodeArgs a) {
                     qf[kk] = v;
                 }
             }
-            float m_run = -INFINITY, l_run = 0.f;
+            // cm_run = c m_run as rounded in the step that raised m_run: when the
+            // max does not rise the exponent of alpha is then exactly 0 and alpha
+            // exactly 1, which lets the PV waves skip the rescale
+            float m_run = -INFINITY, cm_run = -INFINITY, l_run = 0.f;
             f32x16 s = {}, sa = {}, sb = {};
             barrier_lds();   // tile 0 has landed
 
@@ -350,10 +359,13 @@ __global__ void __launch_bounds__(kT, 1) decode64_kernel(const DecodeArgs a) {
                 } else if constexpr (st == 2) {
                     mxa = wave_max_pair(fmaxf(mxa, mxb));   // the two lanes of a head hold disjoint tokens
                 } else if constexpr (st == 3) {
-                    m_new = c * (mxa - m_run) <= a.rescale_tau ? m_run : fmaxf(m_run, mxa);
-                    cm = m_new == -INFINITY ? 0.f : c * m_new;
+                    const bool keep = c * (mxa - m_run) <= a.rescale_tau;
+                    m_new = keep ? m_run : fmaxf(m_run, mxa);
+                    cm = keep ? cm_run : c * m_new;
                 } else if constexpr (st == 4) {
-                    alpha = __builtin_amdgcn_exp2f(c * m_run - cm);
+                    // no score seen yet (cm = -inf): O and l are still 0, alpha 1
+                    alpha = cm == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(cm_run - cm);
+                    cm = cm == -INFINITY ? 0.f : cm;
                 } else if constexpr (st >= 5 && st < 21) {
                     constexpr int r = st - 5;
                     s[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c, -cm));
@@ -365,6 +377,7 @@ __global__ void __launch_bounds__(kT, 1) decode64_kernel(const DecodeArgs a) {
                     psum = wave_sum_pair(psum);
                     l_run = l_run * alpha + psum;
                     m_run = m_new;
+                    cm_run = m_new == -INFINITY ? -INFINITY : cm;
                 } else if constexpr (st == 24) {
 #pragma unroll
                     for (int e = 0; e < 8; ++e) p0[e] = (__bf16)s[e];
@@ -515,19 +528,24 @@ __global__ void __launch_bounds__(kT, 1) decode64_kernel(const DecodeArgs a) {
             // before its first MFMA, the multiplies of block d + 1 placed between
             // the MFMAs of block d.  V fragments are read kPvLA ahead; the order
             // is fixed with scheduling fences.
-            auto pv = [&](int t, float al0, float al1, bool rescale, const bf16x8 (&P)[2][2]) __attribute__((always_inline)) {
-                if (rescale) {
+            auto pv = [&](int t, float al0, float al1, bool rs0, bool rs1, const bf16x8 (&P)[2][2]) __attribute__((always_inline)) {
+                if (rs0) {
 #pragma unroll
-                    for (int r = 0; r < 16; ++r) { acc[0][0][r] *= al0; acc[1][0][r] *= al1; }
+                    for (int r = 0; r < 16; ++r) acc[0][0][r] *= al0;
+                }
+                if (rs1) {
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) acc[1][0][r] *= al1;
                 }
                 __builtin_amdgcn_sched_barrier(0);
                 unroll<0, 8>([&](auto i_c) __attribute__((always_inline)) {
                     constexpr int i = decltype(i_c)::value;
                     constexpr int d = i >> 1, ks = i & 1;
                     const bf16x8 A = fr[i % (kPvLA + 1)];
+                    const bool rs = ks ? rs1 : rs0;
                     acc[0][d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, P[0][ks], acc[0][d], 0, 0, 0);
                     if constexpr (d + 1 < 4) {
-                        if (rescale) {
+                        if (rs) {
 #pragma unroll
                             for (int r = 0; r < 8; ++r) acc[ks][d + 1][r] *= ks ? al1 : al0;
                         }
@@ -535,7 +553,7 @@ __global__ void __launch_bounds__(kT, 1) decode64_kernel(const DecodeArgs a) {
                     __builtin_amdgcn_sched_barrier(0);
                     acc[1][d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, P[1][ks], acc[1][d], 0, 0, 0);
                     if constexpr (d + 1 < 4) {
-                        if (rescale) {
+                        if (rs) {
 #pragma unroll
                             for (int r = 8; r < 16; ++r) acc[ks][d + 1][r] *= ks ? al1 : al0;
                         }
@@ -555,11 +573,15 @@ __global__ void __launch_bounds__(kT, 1) decode64_kernel(const DecodeArgs a) {
 #pragma unroll
                     for (int ks = 0; ks < 2; ++ks) P[hb][ks] = sm.p[ts][hb][ks][l];
                 const float al0 = sm.alpha[ts][0][l & 31], al1 = sm.alpha[ts][1][l & 31];
-                // the rescale is skipped when no head's max rose (alpha = 1 for all)
-                const bool rescale = __builtin_amdgcn_ballot_w64(al0 != 1.f || al1 != 1.f) != 0;
-                pv(t, al0, al1, rescale, P);
+                // a head block's rescale is skipped when none of its heads' max rose
+                // (alpha = 1 for all 32)
+                const bool rs0 = __builtin_amdgcn_ballot_w64(al0 != 1.f) != 0;
+                const bool rs1 = __builtin_amdgcn_ballot_w64(al1 != 1.f) != 0;
+                pv(t, al0, al1, rs0, rs1, P);
                 if (k < sg.n) prefetch(k);
-                barrier_lds();
+                // the prefetch reads stay in flight across the barrier: this wave
+                // writes no LDS, and tile k is not overwritten before step k + 2
+                barrier_only();
             }
             barrier_lds();   // epilogue: fin_inv was written in step n - 1
             // ---- epilogue: normalise and store
