@@ -16,40 +16,56 @@ __global__ void __launch_bounds__(256) combine_kernel(const CombineArgs a) {
     const int h = blockIdx.y * 4 + (threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
     if (h >= a.h_q) return;
-    const int s0 = a.split_offsets[item], s1 = a.split_offsets[item + 1];
+    // split offsets, lse and the float16 scales are uniform per wave: scalar
+    // loads, so the vector loads of the partials are the only memory round trip
+    const int s0 = sload(a.split_offsets + item), s1 = sload(a.split_offsets + item + 1);
     const int n = s1 - s0;
     if (a.skip_single && n == 1) return;
     const int H = a.h_q;
+    const int qd = lane >> 4;   // dims 8 lane .. 8 lane + 7 lie in quarter qd of the head's 512 dims
     // Splits are merged kSplitChunk at a time, every load of a chunk issued
     // before any is used; across chunks the merge is online (running max m).
-    constexpr int kSplitChunk = 4;
+    // Two per chunk: most split items have two or three splits, and the
+    // registers of a larger chunk cost occupancy.
+    constexpr int kSplitChunk = 2;
     float m = -INFINITY, wsum = 0.f;
     float o[8] = {0, 0, 0, 0, 0, 0, 0, 0};
     bool nan_lse = false;   // a split whose softmax sum was NaN (a NaN in q or the cache) makes the row NaN
     for (int k0 = s0; k0 < s1; k0 += kSplitChunk) {
         float lk[kSplitChunk];
-        f32x4 u[kSplitChunk], v[kSplitChunk];
+        float x[kSplitChunk][8];
 #pragma unroll
         for (int c = 0; c < kSplitChunk; ++c) {
             const int k = k0 + c;
             lk[c] = -INFINITY;
-            u[c] = f32x4{0.f, 0.f, 0.f, 0.f};
-            v[c] = u[c];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) x[c][e] = 0.f;
             if (k < s1) {
-                lk[c] = a.lse_part[(int64_t)k * H + h];
+                const int64_t row = (int64_t)k * H + h;
+                lk[c] = sload(a.lse_part + row);
                 if (a.part_fp16) {
                     // float16 partial scaled by 2^-E; dims lane*8 + 0..3 use byte
-                    // 2 q, dims + 4..7 byte 2 q + 1 of the head's exponents (q = lane / 16)
+                    // 2 qd, dims + 4..7 byte 2 qd + 1 of the head's exponents
                     typedef __attribute__((__vector_size__(8 * sizeof(_Float16)))) _Float16 f16x8;
-                    const f16x8 x = *(const f16x8*)((const _Float16*)a.o_part + ((int64_t)k * H + h) * kDv + lane * 8);
-                    const unsigned char* ex = a.o_exp8 + ((int64_t)k * H + h) * 8 + 2 * (lane >> 4);
-                    const int e0 = (int)(signed char)ex[0], e1 = (int)(signed char)ex[1];
-                    u[c] = f32x4{ldexpf((float)x[0], e0), ldexpf((float)x[1], e0), ldexpf((float)x[2], e0), ldexpf((float)x[3], e0)};
-                    v[c] = f32x4{ldexpf((float)x[4], e1), ldexpf((float)x[5], e1), ldexpf((float)x[6], e1), ldexpf((float)x[7], e1)};
+                    const f16x8 v = *(const f16x8*)((const _Float16*)a.o_part + row * kDv + lane * 8);
+                    const uint32_t* ew = (const uint32_t*)(a.o_exp8 + row * 8);
+                    const uint32_t w0 = sload(ew), w1 = sload(ew + 1);
+                    const uint32_t wq = (qd & 2) ? w1 : w0;
+                    const int e0 = (int)(signed char)(wq >> (16 * (qd & 1)));
+                    const int e1 = (int)(signed char)(wq >> (16 * (qd & 1) + 8));
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        x[c][e] = ldexpf((float)v[e], e0);
+                        x[c][e + 4] = ldexpf((float)v[e + 4], e1);
+                    }
                 } else {
-                    const f32x4* src = (const f32x4*)(a.o_part + ((int64_t)k * H + h) * kDv + lane * 8);
-                    u[c] = src[0];
-                    v[c] = src[1];
+                    const f32x4* src = (const f32x4*)(a.o_part + row * kDv + lane * 8);
+                    const f32x4 u = src[0], w = src[1];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        x[c][e] = u[e];
+                        x[c][e + 4] = w[e];
+                    }
                 }
             }
         }
@@ -68,8 +84,8 @@ __global__ void __launch_bounds__(256) combine_kernel(const CombineArgs a) {
         for (int c = 0; c < kSplitChunk; ++c) {
             const float w = lk[c] == -INFINITY ? 0.f : __expf(lk[c] - mc);
             wsum += w;
-            o[0] += w * u[c][0]; o[1] += w * u[c][1]; o[2] += w * u[c][2]; o[3] += w * u[c][3];
-            o[4] += w * v[c][0]; o[5] += w * v[c][1]; o[6] += w * v[c][2]; o[7] += w * v[c][3];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) o[e] += w * x[c][e];
         }
         m = mc;
     }

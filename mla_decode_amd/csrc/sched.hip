@@ -8,15 +8,19 @@
 // The first F cost units of an item carry no tile: they stand for the item's
 // fixed set-up and epilogue work.  num_splits[j] counts the partitions holding
 // tiles of item j; split_offsets is its exclusive prefix sum.
+//
+// The kernel runs once per step ahead of the decode kernel, so its latency is
+// on the step's critical path: four waves, each thread owning a contiguous
+// run of items, and two block scans (wave shuffles plus one LDS exchange).
 
 #include "common.h"
 #include "kernels.h"
 
 namespace mla {
 
-constexpr int kSchedThreads = 1024;
+constexpr int kSchedThreads = 256;
 
-// inclusive block scan of one value per thread (1024 threads, wave64)
+// inclusive scan of one value per thread over the workgroup (4 waves)
 __device__ __forceinline__ int block_scan_incl(int v, int* tmp) {
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
 #pragma unroll
@@ -26,17 +30,8 @@ __device__ __forceinline__ int block_scan_incl(int v, int* tmp) {
     }
     if (lane == 63) tmp[w] = v;
     __syncthreads();
-    if (w == 0) {
-        int t = lane < (kSchedThreads / 64) ? tmp[lane] : 0;
-#pragma unroll
-        for (int o = 1; o < 16; o <<= 1) {
-            const int u = __shfl_up(t, o, 64);
-            if (lane >= o) t += u;
-        }
-        if (lane < (kSchedThreads / 64)) tmp[lane] = t;
-    }
-    __syncthreads();
-    const int add = w > 0 ? tmp[w - 1] : 0;
+    int add = 0;
+    for (int i = 0; i < w; ++i) add += tmp[i];
     __syncthreads();
     return v + add;
 }
@@ -44,53 +39,66 @@ __device__ __forceinline__ int block_scan_incl(int v, int* tmp) {
 __global__ void __launch_bounds__(kSchedThreads) metadata_kernel(const MetaArgs a) {
     __shared__ int C[kMaxMetaItems + 1];    // exclusive prefix sum of item cost
     __shared__ int SO[kMaxMetaItems + 1];   // split offsets
-    __shared__ int tmp[kSchedThreads / 64];
-    __shared__ int carry_s;
     const int N = a.batch * a.s_q;
     const int F = a.fixed_overhead;
     const int P = a.num_parts;
     const int tid = threadIdx.x;
+    __shared__ int tmp[kSchedThreads / 64];
 
     auto tiles_of = [&](int j) -> int {
         if (a.topk > 0) return ((a.cache_seqlens ? topk_slots(a.cache_seqlens[j], a.topk) : a.topk) + 63) >> 6;
         const int b = j / a.s_q, i = j - b * a.s_q;
         return (visible_len(clamp_len(a.cache_seqlens[b], a.max_blocks), a.s_q, i, a.causal) + 63) >> 6;
     };
+    // thread tid owns items [tid * per, tid * per + per)
+    const int per = (N + kSchedThreads - 1) / kSchedThreads;
+    const int j0 = tid * per;
 
     // S1-S2: C_j and T
-    if (tid == 0) { C[0] = 0; carry_s = 0; }
-    __syncthreads();
-    for (int base = 0; base < N; base += kSchedThreads) {
-        const int j = base + tid;
-        const int cost = j < N ? tiles_of(j) + F : 0;
-        const int incl = block_scan_incl(cost, tmp);
-        const int carry = carry_s;
-        if (j < N) C[j + 1] = carry + incl;
-        __syncthreads();
-        if (tid == kSchedThreads - 1) carry_s = carry + incl;
-        __syncthreads();
+    int own = 0;
+    for (int u = 0; u < per; ++u) {
+        const int j = j0 + u;
+        if (j < N) {
+            const int cost = tiles_of(j) + F;
+            C[j + 1] = cost;
+            own += cost;
+        }
     }
+    int run = block_scan_incl(own, tmp) - own;
+    if (tid == 0) C[0] = 0;
+    for (int u = 0; u < per; ++u) {
+        const int j = j0 + u;
+        if (j < N) {
+            run += C[j + 1];
+            C[j + 1] = run;
+        }
+    }
+    __syncthreads();
     const int T = C[N];
     const int q = T > 0 ? (T + P - 1) / P : 1;
 
     // S5: num_splits and split_offsets
-    if (tid == 0) { SO[0] = 0; carry_s = 0; }
-    __syncthreads();
-    for (int base = 0; base < N; base += kSchedThreads) {
-        const int j = base + tid;
-        int ns = 0;
+    own = 0;
+    for (int u = 0; u < per; ++u) {
+        const int j = j0 + u;
         if (j < N) {
             const int n = C[j + 1] - C[j] - F;
             const int first = C[j] + F;
-            ns = n > 0 ? (first + n - 1) / q - first / q + 1 : 0;
+            const int ns = n > 0 ? (first + n - 1) / q - first / q + 1 : 0;
+            SO[j + 1] = ns;
+            own += ns;
         }
-        const int incl = block_scan_incl(ns, tmp);
-        const int carry = carry_s;
-        if (j < N) SO[j + 1] = carry + incl;
-        __syncthreads();
-        if (tid == kSchedThreads - 1) carry_s = carry + incl;
-        __syncthreads();
     }
+    run = block_scan_incl(own, tmp) - own;
+    if (tid == 0) SO[0] = 0;
+    for (int u = 0; u < per; ++u) {
+        const int j = j0 + u;
+        if (j < N) {
+            run += SO[j + 1];
+            SO[j + 1] = run;
+        }
+    }
+    __syncthreads();
 
     int32_t* out = a.meta;
     int32_t* recs = out + kMetaHeader;
