@@ -55,8 +55,16 @@ WARMUP_MIN_S = 0.1
 
 # workload -> (counter summary file, roofline bound)
 COUNTER_FILES = {
-    "dense_b64_s4096": "decode_kernel_dense_b64_h128_s4096_counters.json",
-    "config2": "decode_kernel_dense_b64_h128_s4096_counters.json",
+    "dense_b64_s4096": "decode64_kernel_dense_b64_h128_s4096_counters.json",
+    "config2": "decode64_kernel_dense_b64_h128_s4096_counters.json",
+    "config3": "decode64_kernel_config3_b128_s2_causal_varlen_counters.json",
+    "config4": "decode_kernel_sparse_config4_b64_topk2048_counters.json",
+    "config5": "decode_kernel_fp8_config5_b32_s16384_counters.json",
+    "fp8_sparse_topk2048": "decode_kernel_fp8_sparse_b128_s2_h128_topk2048_counters.json",
+    "fp8_sparse_topk32768": "decode_kernel_fp8_sparse_b128_s2_h128_topk32768_counters.json",
+    "v41_sparse_topk2048": "decode_kernel_fp8_528_sparse_b128_s2_h128_topk2048_counters.json",
+    "fp4_sparse_topk2048": "decode_kernel_fp4_sparse_b128_s2_h128_topk2048_counters.json",
+    "sparse_prefill": "decode_kernel_sparse_prefill_s4096_kv32768_topk2048_counters.json",
 }
 BOUND = {"config1": "hbm", "config2": "hbm", "dense_b64_s4096": "hbm", "config3": "mfma", "config4": "hbm",
          "config5": "mfma"}
@@ -318,6 +326,14 @@ def describe(name, w):
     return f"MLA sparse {kind} decode TFLOPS, µs/step at b=128,s_q=2,h_q=128,topk={topk}{tag} (1 GPU)", cfg, "mfma"
 
 
+def kernel_name(w):
+    """The partial-attention kernel a workload runs (the library's dispatch rule)."""
+    if not w.topk and w.kv_format == "bf16":
+        return "decode64_kernel (dense bf16 cache, 64 heads per workgroup)"
+    fmt = {"bf16": 0, "fp8": 1, "fp8_528": 2, "fp4_288": 3}[w.kv_format]
+    return f"decode_kernel<{'true' if w.topk else 'false'}, {fmt}> (128 heads per workgroup)"
+
+
 def bench_decode(args):
     import torch
     import mla_decode_amd as mla
@@ -377,7 +393,7 @@ def bench_decode(args):
     mfma = {"achieved": round(kern_tflops, 1), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
             "frac": round(kern_tflops / MFMA_BF16_PEAK_TFLOPS, 4), "algorithmic_flops": flops}
     main, other = (hbm, mfma) if bound == "hbm" else (mfma, hbm)
-    roofline = {"bound": bound, "kernel": "partial-attention kernel (decode_kernel), launched as the step launches it",
+    roofline = {"bound": bound, "kernel": kernel_name(w) + ", launched as the step launches it",
                 **{k: main[k] for k in ("achieved", "peak", "unit", "frac")},
                 "traffic": measured_traffic(args.workload), "us_per_launch": round(ms_kernel * 1e3, 2),
                 "us_per_launch_p50": round(_pct(per_kernel, 50) * 1e3, 2)}
@@ -424,16 +440,27 @@ def bench_decode(args):
     print(json.dumps(line), flush=True)
 
 
+PREFILL_SHAPE = (4096, 32768, 128, 2048)   # s_q, s_kv, h_q, topk
+
+
+def prefill_workload(dev):
+    """The prefill workload and its problem: 4096 query rows, the last of a 32768-row bf16 cache, top-k 2048,
+    128 heads."""
+    import mla_decode_amd as mla
+    from workloads import make_sparse_prefill
+    s_q, s_kv, h_q, topk = PREFILL_SHAPE
+    w = make_sparse_prefill(s_q, s_kv, h_q, topk, seed=3000, device=dev)
+    return w, mla.make_problem(1, s_q, h_q, s_kv // 64, topk=topk, softmax_scale=w.softmax_scale)
+
+
 def bench_prefill(args):
     """Top-k sparse prefill: 4096 query rows, the last of a 32768-row bf16 cache, top-k 2048, 128 heads."""
     import types
     import torch
     import mla_decode_amd as mla
-    from workloads import make_sparse_prefill
     dev = torch.device("cuda:0")
-    s_q, s_kv, h_q, topk = 4096, 32768, 128, 2048
-    w = make_sparse_prefill(s_q, s_kv, h_q, topk, seed=3000, device=dev)
-    p = mla.make_problem(1, s_q, h_q, s_kv // 64, topk=topk, softmax_scale=w.softmax_scale)
+    s_q, s_kv, h_q, topk = PREFILL_SHAPE
+    w, p = prefill_workload(dev)
     dec = mla.Decoder(p, dev)
     stream = torch.cuda.current_stream(dev)
     valid = int(((w.indices >= 0) & (w.indices < s_kv)).sum())
@@ -461,9 +488,9 @@ def bench_prefill(args):
                                "top-k 2048 of each row's visible rows, 128 heads, N(0,1) inputs",
                    "s_q": s_q, "s_kv": s_kv, "h_q": h_q, "topk": topk, "d_qk": 576, "d_v": 512,
                    "step": "metadata + sparse prefill (partial + combine when needed)"},
-        "roofline": {"bound": "mfma", "kernel": "partial-attention kernel (decode_kernel<sparse, bf16 cache>)",
+        "roofline": {"bound": "mfma", "kernel": "decode_kernel<true, 0> (128 heads per workgroup)",
                      "achieved": round(kern_tflops, 1), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(kern_tflops / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
+                     "frac": round(kern_tflops / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": measured_traffic("sparse_prefill"),
                      "algorithmic_flops": flops, "us_per_launch": round(ms_kernel * 1e3, 2)},
     }
     if not args.no_cpu_baseline:
@@ -522,13 +549,21 @@ def kernel_only(args):
     import torch
     import mla_decode_amd as mla
     dev = torch.device("cuda:0")
-    w = load_workload(args.workload if args.workload != "sparse_prefill" else "config4", dev)
-    dec = mla.Decoder.for_workload(w, dev)
     stream = torch.cuda.current_stream(dev)
-    dec.metadata(None if w.topk else w.cache_seqlens, stream)
+    if args.workload == "sparse_prefill":
+        w, p = prefill_workload(dev)
+        dec = mla.Decoder(p, dev)
+        dec.metadata(None, stream)
 
-    def k():
-        dec.decode_partial(w.q, w.kv, w.block_table, w.cache_seqlens, w.indices, stream, production=True)
+        def k():
+            dec.decode_partial(w.q, w.kv, None, None, w.indices, stream, production=True)
+    else:
+        w = load_workload(args.workload, dev)
+        dec = mla.Decoder.for_workload(w, dev)
+        dec.metadata(None if w.topk else w.cache_seqlens, stream)
+
+        def k():
+            dec.decode_partial(w.q, w.kv, w.block_table, w.cache_seqlens, w.indices, stream, production=True)
 
     nwarm, _ = _warmup(k, args.warmup)
     ms, per = _timed(k, args.kernel_only, stream)
