@@ -56,6 +56,9 @@ constexpr int kTileB = kSubTok * kRowBytes;     // 36864 bytes per 32-token tile
 constexpr int kRing = 4;                        // LDS tile buffers
 constexpr int kQkLA = 6;                        // K fragments in flight (QK waves)
 constexpr int kPvLA = 4;                        // V fragments in flight (PV waves)
+constexpr int kXRow = 2 * kDv + 16;             // epilogue staging: bytes per head row (16 bytes of bank skew)
+
+typedef __attribute__((__vector_size__(4 * sizeof(_Float16)))) _Float16 f16x4;
 
 // Small arrays first: LDS instructions encode at most a 16-bit immediate
 // offset, so arrays addressed with constant offsets must sit below 64 KiB.
@@ -194,7 +197,7 @@ __global__ void __launch_bounds__(kT, 1) decode64_kernel(const DecodeArgs a) {
     const int lds_tiles = (int)(size_t)(lds_void_t*)&sm.tile[0][0];
 
     // One segment = the tiles of item j that this partition holds.  Every role
-    // walks the same segments and passes the same barriers (n + 5 per segment).
+    // walks the same segments and passes the same barriers (n + 6 per segment).
     struct Seg {
         int nslots, g0, n, slot, b, iq;
         bool final_out, write_ok;
@@ -295,10 +298,12 @@ __global__ void __launch_bounds__(kT, 1) decode64_kernel(const DecodeArgs a) {
                 prefetch_x1(rs, lo + 16384, sink);
             };
             constexpr int kLead = 4;    // step k copies tile k + 2 and prefetches tile k + kLead
+            // tile 0 first: the L2 prefetches of tiles 1 and 2 wait until it has
+            // landed, so that they do not compete with it and with Q at launch
             copy_tile(0);
+            __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): tile 0 has landed
 #pragma unroll
             for (int it = 1; it < kLead - 1; ++it) prefetch_tile(it);
-            __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): tile 0 has landed
             barrier_lds();
             for (int k = -1; k <= sg.n; ++k) {
                 if (k + 2 < sg.n) {
@@ -312,6 +317,7 @@ __global__ void __launch_bounds__(kT, 1) decode64_kernel(const DecodeArgs a) {
             }
             __builtin_amdgcn_s_waitcnt(0x0F70);   // every load of this wave has written LDS
             barrier_lds();   // epilogue
+            barrier_lds();   // epilogue: rows staged in LDS
             barrier_lds();   // the next segment reuses every LDS array
         }
     } else if (is_qk) {
@@ -475,6 +481,7 @@ __global__ void __launch_bounds__(kT, 1) decode64_kernel(const DecodeArgs a) {
             }
             barrier_lds();   // step n
             barrier_lds();   // epilogue
+            barrier_lds();   // epilogue: rows staged in LDS
             barrier_lds();   // the next segment reuses every LDS array
         }
     } else {
@@ -584,51 +591,88 @@ __global__ void __launch_bounds__(kT, 1) decode64_kernel(const DecodeArgs a) {
                 barrier_only();
             }
             barrier_lds();   // epilogue: fin_inv was written in step n - 1
-            // ---- epilogue: normalise and store
-            if (sg.write_ok) {
-                const int l = lane_id64();
-                const int hf = l >> 5;
+            // ---- epilogue: normalise and store.  Two-byte outputs (float16
+            // partials, bf16 output) go through LDS as a row-major 64 x 512
+            // tile, so that every store instruction writes one head's whole
+            // 1 KiB row; the accumulator layout would otherwise spread a store
+            // over 32 rows in 16-byte pieces.  Each format has its own
+            // straight-line code, which keeps the code fetched once per launch
+            // short.
+            const bool part16 = !sg.final_out && a.part_fp16;
+            const bool staged = part16 || (sg.final_out && !a.out_fp32);
+            unsigned char* X = sm.tile[0];
+            const int l = lane_id64();
+            const int hf = l >> 5;
+            // rows of head block hb into X, scaled by sc (per lane: one head)
+            auto stage = [&](auto f16_c, int hb, float sc) __attribute__((always_inline)) {
+                constexpr bool F16 = decltype(f16_c)::value != 0;
+                unsigned char* xp = X + (hb * 32 + (l & 31)) * kXRow + 2 * (128 * dq + 4 * hf);
+#pragma unroll
+                for (int d = 0; d < 4; ++d) {
+#pragma unroll
+                    for (int rq = 0; rq < 4; ++rq) {
+                        const float v0 = acc[hb][d][4 * rq + 0] * sc, v1 = acc[hb][d][4 * rq + 1] * sc;
+                        const float v2 = acc[hb][d][4 * rq + 2] * sc, v3 = acc[hb][d][4 * rq + 3] * sc;
+                        if constexpr (F16) *(f16x4*)(xp + 2 * (32 * d + 8 * rq)) = f16x4{(_Float16)v0, (_Float16)v1, (_Float16)v2, (_Float16)v3};
+                        else *(bf16x4*)(xp + 2 * (32 * d + 8 * rq)) = bf16x4{(__bf16)v0, (__bf16)v1, (__bf16)v2, (__bf16)v3};
+                    }
+                }
+            };
+            if (sg.write_ok && part16) {
+#pragma unroll
+                for (int hb = 0; hb < 2; ++hb) {
+                    const int head = hblk * kH + hb * 32 + (l & 31);
+                    const float inv = sm.fin_inv[hb * 32 + (l & 31)];
+                    float amax = 0.f;
+#pragma unroll
+                    for (int d = 0; d < 4; ++d)
+#pragma unroll
+                        for (int r = 0; r < 16; ++r) amax = fmaxf(amax, fabsf(acc[hb][d][r]));
+                    amax *= inv;
+                    const int be = (int)((__float_as_uint(amax) >> 23) & 0xff);
+                    int E = amax > 0.f ? (be == 0 ? -125 : be - 126) : 0;        // amax * 2^-E < 1
+                    E = E > 127 ? 127 : E;
+                    if (head < H) a.o_exp8[((int64_t)sg.slot * H + head) * 8 + 2 * dq + hf] = (unsigned char)(signed char)E;
+                    stage(Int<1>{}, hb, ldexpf(inv, -E));
+                }
+            } else if (sg.write_ok && staged) {
+#pragma unroll
+                for (int hb = 0; hb < 2; ++hb) stage(Int<0>{}, hb, sm.fin_inv[hb * 32 + (l & 31)]);
+            } else if (sg.write_ok) {
+                // float32 output or partials: stored from the accumulator layout
 #pragma unroll
                 for (int hb = 0; hb < 2; ++hb) {
                     const int head = hblk * kH + hb * 32 + (l & 31);
                     if (head >= H) continue;
                     const float inv = sm.fin_inv[hb * 32 + (l & 31)];
-                    const bool part16 = !sg.final_out && a.part_fp16;
-                    int E = 0;
-                    if (part16) {
-                        float amax = 0.f;
-#pragma unroll
-                        for (int d = 0; d < 4; ++d)
-#pragma unroll
-                            for (int r = 0; r < 16; ++r) amax = fmaxf(amax, fabsf(acc[hb][d][r]));
-                        amax *= inv;
-                        const int be = (int)((__float_as_uint(amax) >> 23) & 0xff);
-                        E = amax > 0.f ? (be == 0 ? -125 : be - 126) : 0;        // amax * 2^-E < 1
-                        E = E > 127 ? 127 : E;
-                        a.o_exp8[((int64_t)sg.slot * H + head) * 8 + 2 * dq + hf] = (unsigned char)(signed char)E;
-                    }
+                    float* base = sg.final_out ? (float*)a.out + ((int64_t)j * H + head) * kDv
+                                               : a.o_part + ((int64_t)sg.slot * H + head) * kDv;
 #pragma unroll
                     for (int d = 0; d < 4; ++d) {
 #pragma unroll
                         for (int rq = 0; rq < 4; ++rq) {
                             const int dim = 128 * dq + 32 * d + 8 * rq + 4 * hf;
-                            const float v0 = acc[hb][d][4 * rq + 0] * inv, v1 = acc[hb][d][4 * rq + 1] * inv;
-                            const float v2 = acc[hb][d][4 * rq + 2] * inv, v3 = acc[hb][d][4 * rq + 3] * inv;
-                            if (part16) {
-                                const int64_t o = ((int64_t)sg.slot * H + head) * kDv + dim;
-                                typedef __attribute__((__vector_size__(4 * sizeof(_Float16)))) _Float16 f16x4;
-                                *(f16x4*)((_Float16*)a.o_part + o) = f16x4{(_Float16)ldexpf(v0, -E), (_Float16)ldexpf(v1, -E),
-                                                                             (_Float16)ldexpf(v2, -E), (_Float16)ldexpf(v3, -E)};
-                            } else if (sg.final_out) {
-                                const int64_t o = ((int64_t)j * H + head) * kDv + dim;
-                                if (a.out_fp32) *(f32x4*)((float*)a.out + o) = f32x4{v0, v1, v2, v3};
-                                else *(bf16x4*)((__bf16*)a.out + o) = bf16x4{(__bf16)v0, (__bf16)v1, (__bf16)v2, (__bf16)v3};
-                            } else {
-                                const int64_t o = ((int64_t)sg.slot * H + head) * kDv + dim;
-                                *(f32x4*)(a.o_part + o) = f32x4{v0, v1, v2, v3};
-                            }
+                            *(f32x4*)(base + dim) = f32x4{acc[hb][d][4 * rq + 0] * inv, acc[hb][d][4 * rq + 1] * inv,
+                                                          acc[hb][d][4 * rq + 2] * inv, acc[hb][d][4 * rq + 3] * inv};
                         }
                     }
+                }
+            }
+            barrier_lds();   // the staged rows are in LDS
+            if (sg.write_ok && staged) {
+                // wave dq stores rows 16 dq .. 16 dq + 15, lane l bytes 16 l .. 16 l + 15
+                const int h0 = hblk * kH + 16 * dq;
+                const int64_t row0 = (part16 ? (int64_t)sg.slot : (int64_t)j) * H + h0;
+                unsigned char* gp = (unsigned char*)a.o_part + 0;
+                if (!part16) gp = (unsigned char*)a.out;
+                gp += row0 * (2 * kDv) + 16 * l;
+                const unsigned char* xp = X + 16 * dq * kXRow + 16 * l;
+                if (h0 + 16 <= H) {
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) *(i32x4*)(gp + i * (2 * kDv)) = *(const i32x4*)(xp + i * kXRow);
+                } else {
+#pragma unroll 1
+                    for (int i = 0; i < H - h0; ++i) *(i32x4*)(gp + i * (2 * kDv)) = *(const i32x4*)(xp + i * kXRow);
                 }
             }
             barrier_lds();   // the next segment reuses every LDS array
