@@ -285,6 +285,11 @@ def load_workload(name, dev):
     return make_fp8_sparse(int(name.split("topk")[1]), device=dev)
 
 
+STEP_DENSE = ("mla_decode_step: schedule computed in the partial-attention kernel (batch * s_q <= 256, else "
+              "the scheduler kernel first), partial attention, combine")
+STEP_SCHED = "mla_decode_step: scheduler kernel, partial attention, combine where an item is split"
+
+
 def describe(name, w):
     """(metric, config dict, roofline bound) of a decode workload."""
     v41 = w.kv_format in ("fp8_528", "fp4_288")
@@ -293,26 +298,26 @@ def describe(name, w):
     if name in ("dense_b64_s4096", "config2"):
         cfg = {"workload": "dense absorbed-MLA decode b=64 s_q=1 h_q=128 seqlen=4096 (64-token pages, "
                            "4096-page shuffled pool, bf16 q/kv N(0,1))", "seqlen": 4096, **base,
-               "step": "metadata + decode (partial + combine)"}
+               "step": STEP_DENSE}
         return METRIC, cfg, "hbm"
     if name == "config1":
         cfg = {"workload": "tiny dense decode b=2 s_q=1 h_q=16 seqlens {200,256}, 8-page pool, fp32 out",
-               **base, "step": "metadata + decode (partial + combine)"}
+               **base, "step": STEP_DENSE}
         return "MLA decode µs/step, tiny dense b=2,h_q=16,seqlens={200,256} (1 GPU)", cfg, "hbm"
     if name == "config3":
         cfg = {"workload": "variable-length speculative decode b=128 s_q=2 causal h_q=128, seqlens uniform in "
                            "[1, 8192], shuffled 64-token pages, bf16 N(0,1)", "causal": True, **base,
-               "step": "metadata + decode (partial + combine)"}
+               "step": STEP_DENSE}
         return "MLA decode TFLOPS, µs/step at b=128,s_q=2 causal,h_q=128,seqlen~U[1,8192] (1 GPU)", cfg, "mfma"
     if name == "config4":
         cfg = {"workload": "DSA top-k sparse decode b=64 s_q=1 h_q=128, top-k 2048 of a 32768-token pool per "
                            "request, 5% of slots -1, bf16 N(0,1)", "topk": w.topk, **base,
-               "step": "metadata + sparse decode (partial + combine)"}
+               "step": STEP_SCHED}
         return "MLA sparse decode TFLOPS, µs/step at b=64,h_q=128,topk=2048 (1 GPU)", cfg, "hbm"
     if name == "config5":
         cfg = {"workload": "FP8 latent-cache decode b=32 s_q=1 h_q=128 seqlen=16384, 656-byte records (512 "
                            "e4m3 + 4 fp32 scales + 64 bf16 RoPE), q bf16 N(0,1)", "seqlen": 16384, **base,
-               "step": "metadata + decode (partial + combine)"}
+               "step": STEP_SCHED}
         return "MLA FP8-cache decode TFLOPS, µs/step at b=32,h_q=128,seqlen=16384 (1 GPU)", cfg, "mfma"
     topk = w.topk
     rec = {"fp8_528": "528-byte records of the 512-wide head (e8m0 scales per 32 values)",
@@ -322,14 +327,16 @@ def describe(name, w):
     kind = "FP4" if w.kv_format == "fp4_288" else "FP8"
     cfg = {"workload": f"{kind} sparse absorbed-MLA decode b=128 s_q=2 h_q=128 top-k {topk} ({rec}, "
                        f"{max(32768, 2 * topk)} cached tokens per request, every slot valid, N(0,1) sources)",
-           "topk": topk, **base, "step": "metadata + sparse decode (partial + combine)"}
+           "topk": topk, **base, "step": STEP_SCHED}
     return f"MLA sparse {kind} decode TFLOPS, µs/step at b=128,s_q=2,h_q=128,topk={topk}{tag} (1 GPU)", cfg, "mfma"
 
 
 def kernel_name(w):
     """The partial-attention kernel a workload runs (the library's dispatch rule)."""
     if not w.topk and w.kv_format == "bf16":
-        return "decode64_kernel (dense bf16 cache, 64 heads per workgroup)"
+        fused = w.batch * w.s_q <= 256
+        return (f"decode64_kernel<{'true' if fused else 'false'}> (dense bf16 cache, 64 heads per workgroup"
+                + (", schedule computed in the kernel)" if fused else ")"))
     fmt = {"bf16": 0, "fp8": 1, "fp8_528": 2, "fp4_288": 3}[w.kv_format]
     return f"decode_kernel<{'true' if w.topk else 'false'}, {fmt}> (128 heads per workgroup)"
 
@@ -349,8 +356,7 @@ def bench_decode(args):
     seqlens = None if w.topk else w.cache_seqlens
 
     def step():
-        dec.metadata(seqlens, stream)
-        dec.decode(w.q, w.kv, w.block_table, w.cache_seqlens, w.indices, stream)
+        dec.step(w.q, w.kv, w.block_table, seqlens, w.indices, stream)
 
     scratch = None
     before = None
@@ -380,7 +386,8 @@ def bench_decode(args):
                           args.steps, stream, before)
     # the dominant kernel alone, in the launch configuration of the step
     ms_kernel, per_kernel = _timed(
-        lambda: dec.decode_partial(w.q, w.kv, w.block_table, w.cache_seqlens, w.indices, stream, production=True),
+        lambda: dec.decode_partial(w.q, w.kv, w.block_table, w.cache_seqlens, w.indices, stream, production=True,
+                                   fused=True),
         args.steps, stream, before)
     ms_meta, _ = _timed(lambda: dec.metadata(seqlens, stream), args.steps, stream)
 
@@ -563,7 +570,8 @@ def kernel_only(args):
         dec.metadata(None if w.topk else w.cache_seqlens, stream)
 
         def k():
-            dec.decode_partial(w.q, w.kv, w.block_table, w.cache_seqlens, w.indices, stream, production=True)
+            dec.decode_partial(w.q, w.kv, w.block_table, w.cache_seqlens, w.indices, stream, production=True,
+                               fused=True)
 
     nwarm, _ = _warmup(k, args.warmup)
     ms, per = _timed(k, args.kernel_only, stream)

@@ -57,7 +57,7 @@
 extern "C" {
 #endif
 
-#define MLA_DECODE_ABI_VERSION 5
+#define MLA_DECODE_ABI_VERSION 6
 
 typedef enum {
     MLA_OK = 0,
@@ -245,7 +245,10 @@ mla_status_t mla_combine(int32_t num_items, int32_t h_q, int32_t s_q, const floa
  * first, then lse_part at float offset max_splits*h_q*512).  partial_format 1:
  * the format mla_decode_fwd itself writes before its combine (float16 scaled
  * per lane by a power of two when the output is bf16, float32 otherwise), so
- * that the launch is the one a decode step makes.  ``table_or_indices`` is
+ * that the launch is the one mla_decode_fwd makes.  partial_format 2: the
+ * launch mla_decode_step makes -- format 1, with the schedule computed inside
+ * the kernel and written to meta->dev where mla_decode_step does that (dense
+ * bf16, batch * s_q <= 256), format 1 otherwise.  ``table_or_indices`` is
  * block_table (dense) or indices (sparse); cache_seqlens is ignored for sparse
  * problems, topk_length for dense ones; attn_sink applies to the outputs this
  * call writes.  Same errors as mla_decode_fwd, plus INVALID_ARG for another
@@ -267,22 +270,43 @@ mla_status_t mla_debug_gather_rows(const mla_problem_t *problem, const int32_t *
                                    const int32_t *cache_seqlens, const int32_t *topk_length,
                                    int32_t *rows_out, void *stream);
 
+/* One whole decode step in a single call: the split-KV schedule for the
+ * current lengths, the partial-attention kernel and the combine.  The pages'
+ * newer interface makes the metadata call a placeholder and lets the first
+ * decode call compute the schedule on the device and keep it for the layers
+ * and steps that follow (FlashMLA deep dive, "tile_scheduler_metadata";
+ * sparse decoding usage note); this call does the same every time it runs and
+ * writes the schedule to meta->dev, so later mla_decode_fwd /
+ * mla_sparse_decode_fwd calls with the same lengths can reuse ``meta``.
+ * Dense bf16 problems with batch * s_q <= 256 compute the schedule inside the
+ * partial-attention kernel (no scheduler launch); every other problem runs
+ * mla_get_decode_metadata first.  Either way meta->dev ends up holding the
+ * words mla_get_decode_metadata would write, and out/lse are bit-identical to
+ * that call followed by the decode call.  Arguments as for those calls:
+ * table_or_indices is block_table (dense, with cache_seqlens) or indices
+ * (sparse, with topk_length optional); ``meta`` comes from mla_plan and must
+ * have meta->dev set.  Errors: theirs. */
+mla_status_t mla_decode_step(const mla_problem_t *problem, const void *q, const void *kv_cache,
+                             const int32_t *table_or_indices, const int32_t *cache_seqlens,
+                             const int32_t *topk_length, const float *attn_sink, const mla_metadata_t *meta,
+                             void *workspace, size_t workspace_bytes, void *out, float *lse, void *stream);
+
 /* For callers that cannot allocate device memory (code under HIP graph
  * capture, tight serving loops, harnesses that forbid hipMalloc): one whole
  * decode step -- mla_plan with ``num_cus`` (0: the device's compute units),
- * the scheduler of mla_get_decode_metadata, then mla_decode_fwd (dense,
- * problem->topk == 0: table_or_indices = block_table, cache_seqlens
- * required) or mla_sparse_decode_fwd (table_or_indices = indices,
+ * then mla_decode_step (dense, problem->topk == 0: table_or_indices =
+ * block_table, cache_seqlens required; sparse: table_or_indices = indices,
  * topk_length optional) -- with the metadata and the split partials in a
  * scratch area the library holds in device memory (128 MiB per device,
  * reserved when the library is loaded on that device and kept until the
  * process ends) instead of a metadata buffer and a workspace.  The caller
- * passes inputs and outputs as for those calls; the call allocates nothing
- * and makes the same kernel launches as that sequence, so its outputs equal
- * theirs bit for bit.  Every call on a device shares that device's scratch:
+ * passes inputs and outputs as for that call; the call allocates nothing
+ * and makes the same kernel launches as mla_decode_step, so its outputs
+ * equal those of mla_decode_step, and of the metadata call followed by the
+ * decode call, bit for bit.  Every call on a device shares that device's scratch:
  * calls that may overlap on one device (different streams, threads or
  * processes without ordering) race and must be serialised by the caller.
- * Errors: those of mla_plan, mla_get_decode_metadata and the decode call;
+ * Errors: those of mla_plan and mla_decode_step;
  * WORKSPACE_TOO_SMALL, before anything touches the device, when the plan
  * needs more than 64 KiB of metadata or more than 128 MiB - 64 KiB of
  * partials (mla_workspace_bytes), e.g. more than about 500 split slots of

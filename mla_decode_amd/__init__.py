@@ -271,8 +271,12 @@ def debug_gather_rows(problem, table_or_indices, cache_seqlens, rows_out, stream
 
 def debug_decode_partial(problem, q, kv_cache, table_or_indices, cache_seqlens, meta, workspace, out, lse,
                          stream=None, topk_length=None, attn_sink=None, production=False):
-    """Test hook: the partial-attention kernel alone (mla_debug_decode_partial).  ``production``: split
-    partials in the decode call's own format (the launch a decode step makes) instead of mla_combine's."""
+    """Test hook: the partial-attention kernel alone (mla_debug_decode_partial).  ``production``: False or 0
+    for mla_combine's float32 partials, True or 1 for the decode call's own format (the launch mla_decode_fwd
+    makes), 2 for the launch mla_decode_step makes (the schedule computed in the kernel where it does that)."""
+    fmt = int(production)
+    if fmt not in (0, 1, 2):
+        raise ValueError("production must be 0, 1 or 2")
     lib = _lib.load()
     _check_q_out(problem, q, out, lse)
     _check_kv(problem, kv_cache, problem.num_blocks * 64)
@@ -285,7 +289,31 @@ def debug_decode_partial(problem, q, kv_cache, table_or_indices, cache_seqlens, 
     _lib.check("mla_debug_decode_partial", lib.mla_debug_decode_partial(
         ctypes.byref(problem), _ptr(q), _ptr(kv_cache), _ptr(table_or_indices), _ptr(cache_seqlens), _ptr(tl),
         _ptr(sink), ctypes.byref(meta), _ptr(workspace), workspace.numel() * workspace.element_size(), _ptr(out), _ptr(lse),
-        1 if production else 0, _stream(stream)))
+        fmt, _stream(stream)))
+
+
+def decode_step(problem, q, kv_cache, table_or_indices, meta, meta_buf, workspace, out, lse, cache_seqlens=None,
+                topk_length=None, attn_sink=None, stream=None):
+    """A whole decode step in one call (mla_decode_step): the schedule for the current lengths, written to
+    ``meta_buf`` as the metadata call would, then the decode.  Dense bf16 problems with batch * s_q <= 256
+    compute the schedule inside the partial-attention kernel."""
+    lib = _lib.load()
+    _check_q_out(problem, q, out, lse)
+    _check_kv(problem, kv_cache, problem.num_blocks * 64)
+    _check_table(problem, table_or_indices, cache_seqlens)
+    _need(meta_buf, "meta_buf", None)
+    if meta_buf.numel() * meta_buf.element_size() < meta.bytes:
+        raise ValueError("meta_buf too small")
+    _need(workspace, "workspace", None)
+    tl, sink = _topk_length(problem, topk_length), _attn_sink(problem.h_q, attn_sink)
+    dense_len = None if problem.topk > 0 else cache_seqlens
+    _on_gpu(q=q, kv_cache=kv_cache, table_or_indices=table_or_indices, cache_seqlens=dense_len, meta_buf=meta_buf,
+            workspace=workspace, out=out, lse=lse, topk_length=tl, attn_sink=sink)
+    meta.dev = meta_buf.data_ptr()
+    _lib.check("mla_decode_step", lib.mla_decode_step(
+        ctypes.byref(problem), _ptr(q), _ptr(kv_cache), _ptr(table_or_indices), _ptr(dense_len), _ptr(tl),
+        _ptr(sink), ctypes.byref(meta), _ptr(workspace), workspace.numel() * workspace.element_size(), _ptr(out),
+        _ptr(lse), _stream(stream)))
 
 
 def decode_step_noalloc(problem, q, kv_cache, table_or_indices, out, lse, cache_seqlens=None, topk_length=None,
@@ -351,12 +379,13 @@ class Decoder:
         get_decode_metadata(self.problem, cache_seqlens, self.meta, self.meta_buf, stream, topk_length)
 
     def decode_partial(self, q, kv_cache, block_table=None, cache_seqlens=None, indices=None, stream=None,
-                       topk_length=None, attn_sink=None, production=False):
+                       topk_length=None, attn_sink=None, production=False, fused=False):
         """The partial-attention kernel alone (test and measurement hook); ``production`` keeps the decode
-        call's own partial format."""
+        call's own partial format, ``fused`` (with production) makes the launch ``step`` makes."""
         toi = indices if self.problem.topk > 0 else block_table
+        fmt = (2 if fused else 1) if production else 0
         debug_decode_partial(self.problem, q, kv_cache, toi, cache_seqlens, self.meta, self.workspace, self.out,
-                             self.lse, stream, topk_length, attn_sink, production)
+                             self.lse, stream, topk_length, attn_sink, fmt)
 
     def decode(self, q, kv_cache, block_table=None, cache_seqlens=None, indices=None, stream=None,
                topk_length=None, attn_sink=None):
@@ -370,8 +399,12 @@ class Decoder:
 
     def step(self, q, kv_cache, block_table=None, cache_seqlens=None, indices=None, stream=None,
              topk_length=None, attn_sink=None):
-        self.metadata(cache_seqlens, stream, topk_length)
-        return self.decode(q, kv_cache, block_table, cache_seqlens, indices, stream, topk_length, attn_sink)
+        """Schedule and decode in one call (mla_decode_step); leaves the schedule in ``meta_buf`` for later
+        ``decode`` calls with the same lengths."""
+        toi = indices if self.problem.topk > 0 else block_table
+        decode_step(self.problem, q, kv_cache, toi, self.meta, self.meta_buf, self.workspace, self.out, self.lse,
+                    cache_seqlens, topk_length, attn_sink, stream)
+        return self.out, self.lse
 
     def capture(self, q, kv_cache, block_table=None, cache_seqlens=None, indices=None, topk_length=None,
                 attn_sink=None):

@@ -10,7 +10,7 @@ import os
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libmla_decode.so")
 
-ABI_VERSION = 5   # MLA_DECODE_ABI_VERSION of the header this binding mirrors
+ABI_VERSION = 6   # MLA_DECODE_ABI_VERSION of the header this binding mirrors
 MLA_OK = 0
 STATUS_NAMES = {0: "MLA_OK", 1: "MLA_ERR_INVALID_ARG", 2: "MLA_ERR_UNSUPPORTED", 3: "MLA_ERR_WORKSPACE_TOO_SMALL",
                 4: "MLA_ERR_METADATA_MISMATCH", 5: "MLA_ERR_HIP"}
@@ -25,7 +25,7 @@ EXPORTED = ("mla_abi_version", "mla_status_string", "mla_plan", "mla_workspace_b
             "mla_get_decode_metadata", "mla_decode_fwd", "mla_sparse_decode_fwd", "mla_sparse_prefill_fwd",
             "mla_combine",
             "mla_debug_gather_rows", "mla_debug_decode_partial", "mla_check_inputs",
-            "mla_decode_step_noalloc")
+            "mla_decode_step", "mla_decode_step_noalloc")
 
 
 class Problem(ctypes.Structure):
@@ -92,6 +92,9 @@ def load():
     lib.mla_check_inputs.restype = ctypes.c_int
     lib.mla_check_inputs.argtypes = [P(Problem), P(Metadata), vp, vp, vp, vp, ctypes.c_int64, ctypes.c_char_p,
                                      ctypes.c_size_t]
+    lib.mla_decode_step.restype = ctypes.c_int
+    lib.mla_decode_step.argtypes = [P(Problem), vp, vp, vp, vp, vp, vp, P(Metadata), vp, ctypes.c_size_t, vp, vp,
+                                    vp]
     lib.mla_decode_step_noalloc.restype = ctypes.c_int
     lib.mla_decode_step_noalloc.argtypes = [P(Problem), i32, vp, vp, vp, vp, vp, vp, vp, vp, vp]
     _lib = lib

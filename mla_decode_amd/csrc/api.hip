@@ -130,11 +130,17 @@ bool sparse_items_whole(const mla_problem_t* p, const mla_metadata_t* m) {
     return q % cost == 0;
 }
 
+// Problems whose decode call computes its own schedule (decode64 kernel, up to
+// four items per lane of one wave).
+bool step_fusable(const mla_problem_t* p) {
+    return uses_decode64(p) && (int64_t)p->batch * p->s_q <= mla::kMaxFusedItems;
+}
+
 mla_status_t run_decode(const mla_problem_t* p, bool sparse, const void* q, const void* kv,
                         const int32_t* block_table, const int32_t* cache_seqlens, const int32_t* indices,
                         const int32_t* topk_length, const float* attn_sink, const mla_metadata_t* meta,
                         void* ws, size_t ws_bytes, void* out, float* lse, void* stream, bool run_combine = true,
-                        int64_t num_rows = 0, bool production_partials = true) {
+                        int64_t num_rows = 0, bool production_partials = true, bool fused = false) {
     mla_status_t st = validate(p);
     if (st != MLA_OK) return st;
     if (sparse != (p->topk > 0)) return MLA_ERR_INVALID_ARG;
@@ -149,8 +155,10 @@ mla_status_t run_decode(const mla_problem_t* p, bool sparse, const void* q, cons
 
     hipStream_t s = (hipStream_t)stream;
     if (mla::debug_enabled()) {
-        st = mla::debug_check_call(p, meta, true, cache_seqlens, sparse ? indices : block_table, topk_length,
-                                   num_rows, s, sparse ? "sparse decode" : "mla_decode_fwd");
+        // a fused call writes the schedule itself: its inputs are checked here,
+        // the schedule after the partial kernel
+        st = mla::debug_check_call(p, meta, !fused, cache_seqlens, sparse ? indices : block_table, topk_length,
+                                   num_rows, s, fused ? "mla_decode_step" : sparse ? "sparse decode" : "mla_decode_fwd");
         if (st != MLA_OK) return st;
     }
 
@@ -187,8 +195,15 @@ mla_status_t run_decode(const mla_problem_t* p, bool sparse, const void* q, cons
     a.max_slots = (int)slots;
     a.scale_log2 = p->softmax_scale * 1.4426950408889634f;
     a.rescale_tau = p->rescale_threshold;
+    a.fused = fused ? 1 : 0;
+    a.meta_out = fused ? (int32_t*)meta->dev : nullptr;
+    a.fixed_overhead = meta->fixed_overhead;
     const hipError_t e = uses_decode64(p) ? mla::launch_decode64(a, s) : mla::launch_decode(a, sparse, p->kv_format, s);
     if (e != hipSuccess) return MLA_ERR_HIP;
+    if (fused && mla::debug_enabled()) {
+        st = mla::debug_check_call(p, meta, true, cache_seqlens, block_table, nullptr, num_rows, s, "mla_decode_step");
+        if (st != MLA_OK) return st;
+    }
 
     mla::CombineArgs c{};
     c.o_part = a.o_part;
@@ -343,11 +358,13 @@ mla_status_t mla_debug_decode_partial(const mla_problem_t* problem, const void* 
                                       const int32_t* topk_length, const float* attn_sink,
                                       const mla_metadata_t* meta, void* workspace, size_t workspace_bytes,
                                       void* out, float* lse, int32_t partial_format, void* stream) {
-    if (!problem || (partial_format != 0 && partial_format != 1)) return MLA_ERR_INVALID_ARG;
+    if (!problem || partial_format < 0 || partial_format > 2) return MLA_ERR_INVALID_ARG;
     const bool sparse = problem->topk > 0;
+    const bool fused = partial_format == 2 && validate(problem) == MLA_OK && step_fusable(problem);
     return run_decode(problem, sparse, q, kv_cache, sparse ? nullptr : table_or_indices,
                       sparse ? nullptr : cache_seqlens, sparse ? table_or_indices : nullptr, topk_length,
-                      attn_sink, meta, workspace, workspace_bytes, out, lse, stream, false, 0, partial_format == 1);
+                      attn_sink, meta, workspace, workspace_bytes, out, lse, stream, false, 0, partial_format >= 1,
+                      fused);
 }
 
 mla_status_t mla_debug_gather_rows(const mla_problem_t* problem, const int32_t* table_or_indices,
@@ -375,6 +392,25 @@ mla_status_t mla_debug_gather_rows(const mla_problem_t* problem, const int32_t* 
     return mla::launch_gather(g, (hipStream_t)stream) == hipSuccess ? MLA_OK : MLA_ERR_HIP;
 }
 
+mla_status_t mla_decode_step(const mla_problem_t* problem, const void* q, const void* kv_cache,
+                             const int32_t* table_or_indices, const int32_t* cache_seqlens,
+                             const int32_t* topk_length, const float* attn_sink, const mla_metadata_t* meta,
+                             void* workspace, size_t workspace_bytes, void* out, float* lse, void* stream) {
+    mla_status_t st = validate(problem);
+    if (st != MLA_OK) return st;
+    const bool sparse = problem->topk > 0;
+    if (!table_or_indices || (!sparse && !cache_seqlens)) return MLA_ERR_INVALID_ARG;
+    if (step_fusable(problem))
+        return run_decode(problem, false, q, kv_cache, table_or_indices, cache_seqlens, nullptr, nullptr, attn_sink,
+                          meta, workspace, workspace_bytes, out, lse, stream, true, 0, true, true);
+    st = mla_get_decode_metadata(problem, sparse ? nullptr : cache_seqlens, sparse ? topk_length : nullptr,
+                                 (mla_metadata_t*)meta, stream);
+    if (st != MLA_OK) return st;
+    return run_decode(problem, sparse, q, kv_cache, sparse ? nullptr : table_or_indices,
+                      sparse ? nullptr : cache_seqlens, sparse ? table_or_indices : nullptr,
+                      sparse ? topk_length : nullptr, attn_sink, meta, workspace, workspace_bytes, out, lse, stream);
+}
+
 mla_status_t mla_decode_step_noalloc(const mla_problem_t* problem, int32_t num_cus, const void* q,
                                      const void* kv_cache, const int32_t* table_or_indices,
                                      const int32_t* cache_seqlens, const int32_t* topk_length,
@@ -391,13 +427,9 @@ mla_status_t mla_decode_step_noalloc(const mla_problem_t* problem, int32_t num_c
     st = device_scratch(&base);
     if (st != MLA_OK) return st;
     m.dev = base;
-    st = mla_get_decode_metadata(problem, sparse ? nullptr : cache_seqlens, sparse ? topk_length : nullptr, &m,
-                                 stream);
-    if (st != MLA_OK) return st;
-    return run_decode(problem, sparse, q, kv_cache, sparse ? nullptr : table_or_indices,
-                      sparse ? nullptr : cache_seqlens, sparse ? table_or_indices : nullptr,
-                      sparse ? topk_length : nullptr, attn_sink, &m, (unsigned char*)base + kScratchMetaBytes,
-                      kScratchBytes - kScratchMetaBytes, out, lse, stream);
+    return mla_decode_step(problem, q, kv_cache, table_or_indices, cache_seqlens, topk_length, attn_sink, &m,
+                           (unsigned char*)base + kScratchMetaBytes, kScratchBytes - kScratchMetaBytes, out, lse,
+                           stream);
 }
 
 mla_status_t mla_check_inputs(const mla_problem_t* problem, const mla_metadata_t* meta, const int32_t* meta_words,

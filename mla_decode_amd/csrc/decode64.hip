@@ -68,7 +68,8 @@ struct __attribute__((aligned(16))) Smem64 {
     float fin_inv[kH];              // epilogue: output scale 1/l (times the sink factor)
     float fin_pad[kH];
     int valid[kRing];               // valid tokens of the tile in each buffer
-    int pad[4];
+    int seg[2];                     // the current segment's output slot and (split count == 1)
+    int pad[2];
     unsigned char pf_sink[256];     // destination of the L2 prefetch loads (never read)
     unsigned char tile[kRing][kTileB];   // 32-token tiles (bf16, swizzled columns, see lds_chunk)
 };
@@ -161,6 +162,7 @@ __device__ __forceinline__ void unroll(F&& f) {
 
 }  // namespace
 
+template <bool FUSED>
 __global__ void __launch_bounds__(kT, 1) decode64_kernel(const DecodeArgs a) {
     __shared__ Smem64 sm;
     const int tid = threadIdx.x;
@@ -184,11 +186,132 @@ __global__ void __launch_bounds__(kT, 1) decode64_kernel(const DecodeArgs a) {
         part = lin / a.n_hblk;
         hblk = lin - part * a.n_hblk;
     }
+    const int N = a.batch * a.s_q;
     const int32_t* rec = a.meta + kMetaHeader + kMetaRec * part;
     const int32_t* so = a.meta + kMetaHeader + kMetaRec * a.num_parts;
-    const int jb = sload(rec + 0), tbeg = sload(rec + 1), je = sload(rec + 2), tend = sload(rec + 3);
-    const int slot0 = sload(rec + 4);
-    const int N = a.batch * a.s_q;
+    // This partition's record: read from the scheduler's metadata, or (fused)
+    // computed here by every wave from the cache lengths with the scheduler's
+    // arithmetic (item costs, their prefix sum cut into equal runs, split
+    // counts and offsets), items ln * fR + u held by lane ln.
+    int jb, tbeg, je, tend, slot0;
+    int fC[4] = {0, 0, 0, 0}, fTl[4] = {0, 0, 0, 0}, fNS[4] = {0, 0, 0, 0}, fSO[4] = {0, 0, 0, 0};
+    int fR = 1, fRs = 0;
+    // uniform read of item j's entry of a lane-distributed array
+    auto item_at = [&](const int (&v)[4], int j) __attribute__((always_inline)) -> int {
+        const int u = j & (fR - 1);
+        const int x = u == 0 ? v[0] : u == 1 ? v[1] : u == 2 ? v[2] : v[3];
+        return __builtin_amdgcn_readlane(x, j >> fRs);
+    };
+    if constexpr (FUSED) {
+        const int ln = (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+        const int F = a.fixed_overhead, P = a.num_parts;
+        fR = N <= 64 ? 1 : N <= 128 ? 2 : 4;
+        fRs = fR == 1 ? 0 : fR == 2 ? 1 : 2;
+        auto scan_incl = [&](int v) __attribute__((always_inline)) -> int {
+#pragma unroll
+            for (int o = 1; o < 64; o <<= 1) {
+                const int t = __shfl_up(v, o, 64);
+                if (ln >= o) v += t;
+            }
+            return v;
+        };
+        int own = 0;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            if (u < fR) {
+                const int j = ln * fR + u;
+                if (j < N) {
+                    const int b = j / a.s_q, i = j - b * a.s_q;
+                    fTl[u] = (visible_len(clamp_len(a.cache_seqlens[b], a.max_blocks), a.s_q, i, a.causal) + 63) >> 6;
+                    own += fTl[u] + F;
+                }
+            }
+        }
+        int incl = scan_incl(own);
+        const int T = __builtin_amdgcn_readlane(incl, 63);
+        int run = incl - own;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            fC[u] = run;
+            if (u < fR && ln * fR + u < N) run += fTl[u] + F;
+        }
+        const int q = T > 0 ? (T + P - 1) / P : 1;
+        // x / q for 0 <= x < 2^31: a double-precision estimate, exact after one correction
+        const double rq = 1.0 / (double)q;
+        auto div_q = [&](int x) __attribute__((always_inline)) -> int {
+            int d = (int)((double)x * rq);
+            d -= d * q > x ? 1 : 0;
+            d += (d + 1) * q <= x ? 1 : 0;
+            return d;
+        };
+        own = 0;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            if (u < fR) {
+                const int j = ln * fR + u;
+                const int n = fTl[u], first = fC[u] + F;
+                fNS[u] = (j < N && n > 0) ? div_q(first + n - 1) - div_q(first) + 1 : 0;
+                own += fNS[u];
+            }
+        }
+        incl = scan_incl(own);
+        const int total = __builtin_amdgcn_readlane(incl, 63);
+        run = incl - own;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            fSO[u] = run;
+            run += fNS[u];
+        }
+        // last item j with C[j] <= x: the C[j] are non-decreasing, so count them
+        auto item_of = [&](int x) __attribute__((always_inline)) -> int {
+            int cnt = 0;
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+                if (u < fR) cnt += __builtin_popcountll(__builtin_amdgcn_ballot_w64(ln * fR + u < N && fC[u] <= x));
+            return cnt - 1;
+        };
+        const int64_t lo64 = (int64_t)part * q;
+        const int64_t hi64 = lo64 + q < T ? lo64 + q : T;
+        if (lo64 >= hi64) {
+            jb = N; tbeg = 0; je = N; tend = 0; slot0 = 0;
+        } else {
+            const int lo = (int)lo64, hi = (int)hi64;
+            jb = item_of(lo);
+            je = item_of(hi - 1);
+            const int Cjb = item_at(fC, jb), njb = item_at(fTl, jb);
+            const int Cje = item_at(fC, je), nje = item_at(fTl, je);
+            tbeg = lo - Cjb - F;
+            if (tbeg < 0) tbeg = 0;
+            tend = hi - Cje - F;
+            tend = tend < 0 ? 0 : (tend > nje ? nje : tend);
+            const int first_end = je == jb ? tend : njb;
+            slot0 = tbeg < first_end ? item_at(fSO, jb) + part - (Cjb + F) / q : 0;
+        }
+        // the schedule written back in the scheduler's layout: each partition's
+        // record by its first head block, header and split offsets by
+        // workgroup 0 (copy wave 0 of each)
+        if (is_copy && cw == 0) {
+            int32_t* mo = a.meta_out;
+            if (hblk == 0 && ln == 0) {
+                int32_t* r = mo + kMetaHeader + kMetaRec * part;
+                r[0] = jb; r[1] = tbeg; r[2] = je; r[3] = tend; r[4] = slot0;
+            }
+            if (blockIdx.x == 0) {
+                int32_t* so_o = mo + kMetaHeader + kMetaRec * P;
+#pragma unroll
+                for (int u = 0; u < 4; ++u)
+                    if (u < fR && ln * fR + u < N) so_o[ln * fR + u] = fSO[u];
+                if (ln == 0) {
+                    so_o[N] = total;
+                    mo[0] = kMetaMagic; mo[1] = P; mo[2] = N; mo[3] = F;
+                    mo[4] = q; mo[5] = T; mo[6] = a.s_q; mo[7] = T - N * F;
+                }
+            }
+        }
+    } else {
+        jb = sload(rec + 0), tbeg = sload(rec + 1), je = sload(rec + 2), tend = sload(rec + 3);
+        slot0 = sload(rec + 4);
+    }
     const int H = a.h_q;
     const float c = a.scale_log2;
     const unsigned char* kv = (const unsigned char*)a.kv;
@@ -198,6 +321,9 @@ __global__ void __launch_bounds__(kT, 1) decode64_kernel(const DecodeArgs a) {
 
     // One segment = the tiles of item j that this partition holds.  Every role
     // walks the same segments and passes the same barriers (n + 6 per segment).
+    // The copy waves look up its output slot and split count and publish them
+    // in LDS before the segment's first barrier; the other roles read them at
+    // the segment's end.
     struct Seg {
         int nslots, g0, n, slot, b, iq;
         bool final_out, write_ok;
@@ -209,15 +335,30 @@ __global__ void __launch_bounds__(kT, 1) decode64_kernel(const DecodeArgs a) {
         int t1 = (j == je) ? tend : ntile_j;
         if (t1 > ntile_j) t1 = ntile_j;
         if (t0 >= t1) return false;
-        const int nsplit = sload(so + j + 1) - sload(so + j);
-        sg.slot = (j == jb) ? slot0 : sload(so + j);
         sg.g0 = 2 * t0;                                                     // first 32-token tile
         sg.n = min(2 * t1, (sg.nslots + kSubTok - 1) / kSubTok) - sg.g0;   // tiles of this segment
-        sg.final_out = nsplit == 1;
-        sg.write_ok = sg.final_out || (sg.slot >= 0 && sg.slot < a.max_slots);
         sg.b = j / a.s_q;
         sg.iq = j - sg.b * a.s_q;
         return true;
+    };
+    // copy waves: slot and split count of segment j
+    auto seg_split = [&](int j, Seg& sg) __attribute__((always_inline)) {
+        int nsplit;
+        if constexpr (FUSED) {
+            nsplit = item_at(fNS, j);
+            sg.slot = (j == jb) ? slot0 : item_at(fSO, j);
+        } else {
+            nsplit = sload(so + j + 1) - sload(so + j);
+            sg.slot = (j == jb) ? slot0 : sload(so + j);
+        }
+        sg.final_out = nsplit == 1;
+        sg.write_ok = sg.final_out || (sg.slot >= 0 && sg.slot < a.max_slots);
+    };
+    // QK and PV waves, after the segment's first barrier
+    auto seg_read = [&](Seg& sg) __attribute__((always_inline)) {
+        sg.slot = __builtin_amdgcn_readfirstlane(sm.seg[0]);
+        sg.final_out = __builtin_amdgcn_readfirstlane(sm.seg[1]) != 0;
+        sg.write_ok = sg.final_out || (sg.slot >= 0 && sg.slot < a.max_slots);
     };
 
     if (is_copy) {
@@ -225,6 +366,9 @@ __global__ void __launch_bounds__(kT, 1) decode64_kernel(const DecodeArgs a) {
         for (int j = jb; j <= je && j < N; ++j) {
             Seg sg;
             if (!segment(j, sg)) continue;
+            seg_split(j, sg);
+            sm.seg[0] = sg.slot;
+            sm.seg[1] = sg.final_out ? 1 : 0;
             const int npages_item = (sg.nslots + kBlock - 1) / kBlock;
             int pt_base = 0, pt_v = 0;
             auto load_pages = [&](int first) __attribute__((always_inline)) {
@@ -447,23 +591,23 @@ __global__ void __launch_bounds__(kT, 1) decode64_kernel(const DecodeArgs a) {
                 }
             };
             // The valid token count of tile k is written with its copy in step
-            // k - 2 and read in step k - 1, so no step starts with a wait for it.
-            auto valid_of = [&](int t) __attribute__((always_inline)) -> int {
-                return __builtin_amdgcn_readfirstlane(sm.valid[t % kRing]);
-            };
+            // k - 2; step k - 1 asks for it with its first fragment reads and
+            // uses it at its end, so the read's latency is hidden.
             // step -1: QK(0)
-            qk(0, Int<0>{}, 0, [] {});
-            int nv = valid_of(0);
+            int nv_raw = 0;
+            qk(0, Int<0>{}, 0, [&] { nv_raw = sm.valid[0]; });
+            int nv = __builtin_amdgcn_readfirstlane(nv_raw);
             barrier_lds();
             // steps 0 .. n-2: softmax(k) and QK(k+1)
             for (int k = 0; k + 1 < sg.n; ++k) {
-                qk(k + 1, Int<1>{}, k & 1, [&] { scores(nv); });
-                nv = valid_of(k + 1);
+                qk(k + 1, Int<1>{}, k & 1, [&] { scores(nv); nv_raw = sm.valid[(k + 1) % kRing]; });
+                nv = __builtin_amdgcn_readfirstlane(nv_raw);
                 barrier_lds();
             }
             // step n-1: the last softmax, then the output scale and lse
             {
                 const int k = sg.n - 1;
+                seg_read(sg);
                 scores(nv);
                 unroll<0, kSoftStages>([&](auto st_c) __attribute__((always_inline)) { soft_stage(st_c, k & 1); });
                 const int l = lane_id64();
@@ -591,6 +735,7 @@ __global__ void __launch_bounds__(kT, 1) decode64_kernel(const DecodeArgs a) {
                 barrier_only();
             }
             barrier_lds();   // epilogue: fin_inv was written in step n - 1
+            seg_read(sg);
             // ---- epilogue: normalise and store.  Two-byte outputs (float16
             // partials, bf16 output) go through LDS as a row-major 64 x 512
             // tile, so that every store instruction writes one head's whole
@@ -681,7 +826,8 @@ __global__ void __launch_bounds__(kT, 1) decode64_kernel(const DecodeArgs a) {
 }
 
 hipError_t launch_decode64(const DecodeArgs& a, hipStream_t stream) {
-    hipLaunchKernelGGL(decode64_kernel, dim3(a.num_parts * a.n_hblk), dim3(kT), 0, stream, a);
+    if (a.fused) hipLaunchKernelGGL(decode64_kernel<true>, dim3(a.num_parts * a.n_hblk), dim3(kT), 0, stream, a);
+    else hipLaunchKernelGGL(decode64_kernel<false>, dim3(a.num_parts * a.n_hblk), dim3(kT), 0, stream, a);
     return hipGetLastError();
 }
 

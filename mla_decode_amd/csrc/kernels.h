@@ -27,6 +27,9 @@ struct DecodeArgs {
     int num_parts, n_hblk, max_slots;
     float scale_log2;            // softmax_scale * log2(e)
     float rescale_tau;           // running-max threshold in log2 units (0 = exact running max)
+    int32_t* meta_out;           // fused: the schedule computed in the kernel is written here (same layout)
+    int fused;                   // decode64: compute the schedule in the kernel instead of reading meta
+    int fixed_overhead;          // fused: the scheduler's per-item cost F
 };
 
 struct MetaArgs {
@@ -65,5 +68,6 @@ hipError_t launch_combine(const CombineArgs& a, hipStream_t stream);
 hipError_t launch_gather(const GatherArgs& a, hipStream_t stream);
 
 constexpr int kMaxMetaItems = 16384;   // batch * s_q handled by the one-workgroup scheduler
+constexpr int kMaxFusedItems = 256;    // batch * s_q the decode64 kernel schedules itself (4 per lane)
 
 }  // namespace mla

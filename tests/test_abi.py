@@ -35,7 +35,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_abi_version_and_status_strings(lib):
-    assert lib.mla_abi_version() == 5
+    assert lib.mla_abi_version() == 6
     for s in range(6):
         assert lib.mla_status_string(s)
     assert lib.mla_status_string(99) == b"unknown status"
@@ -176,3 +176,28 @@ def test_noalloc_step_rejects_oversized_plans_before_touching_the_device(lib):
     p = _problem(batch=0)
     assert lib.mla_decode_step_noalloc(ctypes.byref(p), 256, fake, fake, fake, fake, None, None, fake, fake,
                                        None) == 1
+
+
+def test_decode_step_rejects_bad_arguments_before_touching_the_device(lib):
+    import mla_decode_amd as mla
+    fake = ctypes.c_void_p(1 << 20)       # never dereferenced: every call below fails on the host
+    p = _problem()
+    m = mla.plan(p, num_cus=256)
+    m.dev = 1 << 20
+    ws = mla._lib.load().mla_workspace_bytes(ctypes.byref(m))
+    step = lib.mla_decode_step
+    # no block table
+    assert step(ctypes.byref(p), fake, fake, None, fake, None, None, ctypes.byref(m), fake, ws, fake, fake,
+                None) == 1
+    # metadata planned for another problem
+    other = mla.plan(_problem(batch=32), num_cus=256)
+    other.dev = 1 << 20
+    assert step(ctypes.byref(p), fake, fake, fake, fake, None, None, ctypes.byref(other), fake, ws, fake, fake,
+                None) == 4
+    # workspace smaller than the plan needs
+    assert step(ctypes.byref(p), fake, fake, fake, fake, None, None, ctypes.byref(m), fake, ws - 16, fake, fake,
+                None) == 3
+    # sparse: the scheduler call checks the metadata first
+    ps = _problem(topk=2048)
+    assert step(ctypes.byref(ps), fake, fake, fake, None, None, None, ctypes.byref(other), fake, ws, fake, fake,
+                None) == 4

@@ -1,0 +1,84 @@
+"""The one-call decode step (mla_decode_step).  For dense bf16 problems of up
+to 256 query tokens the schedule is computed inside the partial-attention
+kernel; the metadata buffer it leaves must hold word for word what the
+scheduler kernel writes for the same lengths, and out/lse must equal, bit for
+bit, those of the metadata call followed by the decode call.  The cases cover
+one, two and four items per lane of the in-kernel scan, empty and one-token
+requests, partitions spanning many short requests, three head blocks, and a
+batch past the fused limit (scheduler kernel first)."""
+
+import numpy as np
+import pytest
+import torch
+
+from workloads import make_dense
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import mla_decode_amd._lib as L
+    L.load()   # fails loudly if the HIP library is missing
+
+
+def _lens(n, lo, hi, seed):
+    r = np.random.default_rng(seed)
+    return [int(x) for x in r.integers(lo, hi + 1, size=n)]
+
+
+CASES = {
+    "b2_h16": lambda: make_dense(2, 1, 16, [200, 256], seed=1, device=DEV),
+    "b64_equal": lambda: make_dense(64, 1, 128, [1024] * 64, seed=2, device=DEV),
+    "b65_varlen_with_empty": lambda: make_dense(65, 1, 128, [0, 1] + _lens(63, 0, 900, 3), seed=3, device=DEV),
+    "b100_s2_causal": lambda: make_dense(100, 2, 128, _lens(100, 1, 700, 4), causal=True, seed=4, device=DEV),
+    "b128_s2_causal": lambda: make_dense(128, 2, 128, _lens(128, 64, 600, 5), causal=True, seed=5, device=DEV),
+    "b200_short": lambda: make_dense(200, 1, 64, _lens(200, 0, 130, 6), seed=6, device=DEV),
+    "b3_h192_causal": lambda: make_dense(3, 2, 192, [1, 300, 777], causal=True, seed=7, device=DEV),
+    "b300_not_fused": lambda: make_dense(300, 1, 32, _lens(300, 1, 200, 8), seed=8, device=DEV),
+}
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_step_matches_metadata_then_decode(name):
+    import mla_decode_amd as mla
+    print(f"decode step: {name}", flush=True)
+    w = CASES[name]()
+    dec = mla.Decoder.for_workload(w, DEV)
+    words = dec.meta.bytes // 4
+    dec.metadata(w.cache_seqlens)
+    ref_meta = dec.meta_buf.view(torch.int32)[:words].clone()
+    o1, l1 = dec.decode(w.q, w.kv, w.block_table, w.cache_seqlens)
+    o1, l1 = o1.clone(), l1.clone()
+    dec.meta_buf.fill_(-7)
+    dec.out.fill_(float("nan"))
+    dec.lse.fill_(float("nan"))
+    o2, l2 = dec.step(w.q, w.kv, w.block_table, w.cache_seqlens)
+    torch.cuda.synchronize()
+    got_meta = dec.meta_buf.view(torch.int32)[:words]
+    assert torch.equal(got_meta, ref_meta), (got_meta - ref_meta).nonzero()[:8].tolist()
+    assert torch.equal(o1, o2)
+    assert torch.equal(l1, l2)
+    # the schedule left behind serves a later decode call with the same lengths
+    o3, l3 = dec.decode(w.q, w.kv, w.block_table, w.cache_seqlens)
+    assert torch.equal(o1, o3) and torch.equal(l1, l3)
+
+
+def test_step_follows_new_lengths():
+    import mla_decode_amd as mla
+    print("decode step: lengths change between calls", flush=True)
+    w = make_dense(64, 1, 128, _lens(64, 100, 2000, 9), seed=9, device=DEV, max_blocks=40)
+    dec = mla.Decoder.for_workload(w, DEV)
+    dec.step(w.q, w.kv, w.block_table, w.cache_seqlens)
+    shorter = (w.cache_seqlens // 2).contiguous()
+    o2, l2 = dec.step(w.q, w.kv, w.block_table, shorter)
+    o2, l2 = o2.clone(), l2.clone()
+    m2 = dec.meta_buf.clone()
+    dec.metadata(shorter)
+    assert torch.equal(dec.meta_buf, m2)
+    o3, l3 = dec.decode(w.q, w.kv, w.block_table, shorter)
+    assert torch.equal(o2, o3) and torch.equal(l2, l3)
