@@ -2,6 +2,7 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+#include <stddef.h>
 #include <stdint.h>
 
 namespace mla {
@@ -50,6 +51,19 @@ template <class T>
 __device__ __forceinline__ T sload(const T* p) {
     return *(const __attribute__((address_space(4))) T*)(p);
 }
+
+// A field of the kernel's argument struct (which sits at offset 0 of the
+// kernarg segment), loaded where it is used: the asm hides the pointer from
+// the optimiser, so the load is not hoisted to the kernel's start and the
+// value holds no scalar register across the kernel's main loop.
+template <class T>
+__device__ __forceinline__ T kernarg_at(size_t off) {
+    const __attribute__((address_space(4))) char* p =
+        (const __attribute__((address_space(4))) char*)__builtin_amdgcn_kernarg_segment_ptr();
+    __asm__ volatile("" : "+s"(p));
+    return *(const __attribute__((address_space(4))) T*)(p + off);
+}
+#define MLA_LATE_ARG(Struct, field) mla::kernarg_at<decltype(Struct::field)>(offsetof(Struct, field))
 
 __host__ __device__ __forceinline__ int visible_len(int L, int s_q, int i, int causal) {
     if (!causal) return L;

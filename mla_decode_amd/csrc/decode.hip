@@ -379,7 +379,10 @@ __global__ void __launch_bounds__(kThreads, 1) decode_kernel(const DecodeArgs a)
     }
 
     const int32_t* rec = a.meta + kMetaHeader + kMetaRec * part;
-    const int32_t* so = a.meta + kMetaHeader + kMetaRec * a.num_parts;
+    // split offsets, read once per segment from a pointer loaded there
+    auto so_at = [&](int k) __attribute__((always_inline)) -> int {
+        return sload(MLA_LATE_ARG(DecodeArgs, meta) + kMetaHeader + kMetaRec * MLA_LATE_ARG(DecodeArgs, num_parts) + k);
+    };
     const int jb = sload(rec + 0), tbeg = sload(rec + 1), je = sload(rec + 2), tend = sload(rec + 3);
     const int slot0 = sload(rec + 4);
     const int N = a.batch * a.s_q;
@@ -394,9 +397,15 @@ __global__ void __launch_bounds__(kThreads, 1) decode_kernel(const DecodeArgs a)
     const int head = hblk * kHeadsPerWG + hb * 32 + l32;   // this lane's head
     const bool head_ok = head < H;
 
-    const int ftok = l32 ^ (4 * half + 8 * (wave & 1));   // bf16 fill: token this lane copies
-    const int fbase = ftok * kRowBytes + 16 * half;       // dense fill source offset (+32k)
-    const int fcol = 16 * half;                            // sparse fill column offset (+32k)
+    // bf16 fill: the token a lane copies, its dense source offset (+32k) and its
+    // sparse column offset (+32k), rebuilt from the lane id where used so that
+    // they are not held across the tile loop
+    auto ftok = [&]() __attribute__((always_inline)) -> int {
+        const int ln = lane_id();
+        return (ln & 31) ^ (4 * (ln >> 5) + 8 * (wave & 1));
+    };
+    auto fbase = [&]() __attribute__((always_inline)) -> int { return ftok() * kRowBytes + 16 * (lane_id() >> 5); };
+    auto fcol = [&]() __attribute__((always_inline)) -> int { return 16 * (lane_id() >> 5); };
 
     // LDS byte offsets inside a tile (see lds_chunk).  K operand: token l32,
     // column 32kh + 2kk + half -> kb[kk & 1] + 1024 kk + 16384 kh.  V^T
@@ -418,14 +427,19 @@ __global__ void __launch_bounds__(kThreads, 1) decode_kernel(const DecodeArgs a)
     }
 
     for (int j = jb; j <= je && j < N; ++j) {
-        const int nslots = rr.slots_uniform(j);
+        // the item's length, read with s_q loaded here (a divisor held across the
+        // tile loop would keep its reciprocal in scalar registers)
+        const int sq_s = MLA_LATE_ARG(DecodeArgs, s_q);
+        const RowResolver rrs{nullptr, SPARSE ? MLA_LATE_ARG(DecodeArgs, topk_length) : MLA_LATE_ARG(DecodeArgs, cache_seqlens),
+                              nullptr, sq_s, a.max_blocks, SPARSE ? a.topk : 0, a.causal, a.num_rows};
+        const int nslots = rrs.slots_uniform(j);
         const int ntile_j = (nslots + 63) >> 6;
         const int t0 = (j == jb && tbeg > 0) ? tbeg : 0;
         int t1 = (j == je) ? tend : ntile_j;
         if (t1 > ntile_j) t1 = ntile_j;
         if (t0 >= t1) continue;
-        const int nsplit = sload(so + j + 1) - sload(so + j);
-        const int slot = (j == jb) ? slot0 : sload(so + j);
+        const int nsplit = so_at(j + 1) - so_at(j);
+        const int slot = (j == jb) ? slot0 : so_at(j);
         const int g0 = 2 * t0;                                    // first 32-token tile
         const int gend = min(2 * t1, (nslots + kSubTok - 1) / kSubTok);
         const int ns = gend - g0;
@@ -434,13 +448,13 @@ __global__ void __launch_bounds__(kThreads, 1) decode_kernel(const DecodeArgs a)
         // dense: page ids of 64 consecutive pages of item j, one per lane, read
         // with v_readlane.  A scalar load here would be waited for with
         // lgkmcnt(0), which also drains every outstanding LDS operation.
-        const int b_item = j / a.s_q;
+        const int b_item = j / sq_s;
         const int npages_item = (nslots + kBlock - 1) / kBlock;
         int pt_base = g0 >> 1, pt_v = 0;
         auto load_pages = [&](int first) __attribute__((always_inline)) {
             pt_base = first;
             const int pi = first + lane;
-            pt_v = pi < npages_item ? a.block_table[(int64_t)b_item * a.max_blocks + pi] : 0;
+            pt_v = pi < npages_item ? MLA_LATE_ARG(DecodeArgs, block_table)[(int64_t)b_item * a.max_blocks + pi] : 0;
             // waited for here, so that no later read of pt_v waits for other loads
             __builtin_amdgcn_s_waitcnt(0x0F70);
         };
@@ -457,7 +471,7 @@ __global__ void __launch_bounds__(kThreads, 1) decode_kernel(const DecodeArgs a)
             const int tid_o = wave * 64 + lane_id();
             const int head_o = hblk * kHeadsPerWG + hb * 32 + (tid_o & 31);
             const int half_o = (tid_o >> 5) & 1;
-            const bf16x8* qp = (const bf16x8*)((const unsigned char*)a.q +
+            const bf16x8* qp = (const bf16x8*)((const unsigned char*)MLA_LATE_ARG(DecodeArgs, q) +
                                                ((int64_t)j * H + (head_o < H ? head_o : 0)) * kQRow);
 #pragma unroll
             for (int kk = 0; kk < 16; ++kk) {
@@ -472,7 +486,7 @@ __global__ void __launch_bounds__(kThreads, 1) decode_kernel(const DecodeArgs a)
                 const int hq = hblk * kHeadsPerWG + hb2 * 32 + (ln & 31);
                 bf16x8 v = {};
                 if (!D512 && hq < H)
-                    v = ((const bf16x8*)((const unsigned char*)a.q + ((int64_t)j * H + hq) * kQRow))[64 + 2 * kr + (ln >> 5)];
+                    v = ((const bf16x8*)((const unsigned char*)MLA_LATE_ARG(DecodeArgs, q) + ((int64_t)j * H + hq) * kQRow))[64 + 2 * kr + (ln >> 5)];
                 qrv[e] = v;
             }
         }
@@ -480,7 +494,11 @@ __global__ void __launch_bounds__(kThreads, 1) decode_kernel(const DecodeArgs a)
         f32x16 acc[8];
 #pragma unroll
         for (int d = 0; d < 8; ++d) acc[d] = f32x16{};
-        float m_run = -INFINITY, l_run = 0.f;
+        // cm_run: the running max of the scores times c (c > 0), as rounded in
+        // the step that raised it.  When the max does not rise the exponent of
+        // alpha is exactly 0 and alpha exactly 1, which lets the rescale be
+        // skipped.
+        float cm_run = -INFINITY, l_run = 0.f;
 
         int pg0 = 0, pg1 = 0, pg2 = 0;
         if (!SPARSE) {
@@ -498,7 +516,7 @@ __global__ void __launch_bounds__(kThreads, 1) decode_kernel(const DecodeArgs a)
         auto issue_fill = [&](int it, int page) __attribute__((always_inline)) {
             const int g = g0 + it;
             const int dst = (int)(size_t)(lds_void_t*)&sm.tile[0][0] + opaque_tile_offset(it % kNBuf);
-            if (SPARSE) fill_sparse(dst, bf16_row_addr(kv, sm.rows[it & 3][ftok], fcol + 32 * wave), wave);
+            if (SPARSE) fill_sparse(dst, bf16_row_addr(kv, sm.rows[it & 3][ftok()], fcol() + 32 * wave), wave);
             else {
                 const int ln = lane_id();
                 const int fb = ((ln & 31) ^ (4 * (ln >> 5) + 8 * (wave & 1))) * kRowBytes + 16 * (ln >> 5);
@@ -554,7 +572,7 @@ __global__ void __launch_bounds__(kThreads, 1) decode_kernel(const DecodeArgs a)
         }
 #pragma unroll
         for (int e = 0; e < 2; ++e) {
-            const int idx = tid + kThreads * e;
+            const int idx = wave * 64 + lane_id() + kThreads * e;   // lane term rebuilt here, not held
             if (!D512) sm.qr[idx >> 8][(idx >> 6) & 3][idx & 63] = qrv[e];
         }
         if (!FP8) __builtin_amdgcn_s_waitcnt(0x0F70);
@@ -592,17 +610,17 @@ __global__ void __launch_bounds__(kThreads, 1) decode_kernel(const DecodeArgs a)
             const bool live = t + 1 < ns;
             f.l0 = (int)(size_t)(lds_void_t*)&sm.tile[0][0] + opaque_tile_offset((t + 1) % kNBuf) + 1024 * w;
             if (SPARSE) {
-                f.src = bf16_row_addr(kv, live ? sm.rows[(t + 1) & 3][ftok] : -1, fcol + 32 * w);
+                f.src = bf16_row_addr(kv, live ? sm.rows[(t + 1) & 3][ftok()] : -1, fcol() + 32 * w);
             } else if (!live) {
                 f.rs = buffer_rsrc(kv, 0, 0);
-                f.vo = fbase + 32 * w;
+                f.vo = fbase() + 32 * w;
             } else {
                 const bool ok = page_ok(pg1, a.num_rows);
                 int nvalid = min(nslots - g * kSubTok, kSubTok);
                 if (!ok || nvalid < 0) nvalid = 0;
                 f.rs = buffer_rsrc(kv + (ok ? (int64_t)pg1 * kTileBytes + (g & 1) * kSubBytes : 0), 0,
                                    nvalid * kRowBytes);
-                f.vo = fbase + 32 * w;
+                f.vo = fbase() + 32 * w;
             }
             return f;
         };
@@ -729,10 +747,12 @@ __global__ void __launch_bounds__(kThreads, 1) decode_kernel(const DecodeArgs a)
             // Running max: raised to the tile max only when that exceeds it by
             // more than tau in log2 units (tau = 0: whenever it is larger,
             // the exact running max).  From -inf any finite max is taken.
-            const float m_new = c * (mx - m_run) <= a.rescale_tau ? m_run : fmaxf(m_run, mx);
-            // while every score so far is masked, m_new = -inf: p = exp2(-inf) = 0
-            const float cm = m_new == -INFINITY ? 0.f : c * m_new;
-            const float alpha = __builtin_amdgcn_exp2f(c * m_run - cm);
+            const float cmx = c * mx;
+            const bool keep = cmx - cm_run <= a.rescale_tau;
+            const float cm_new = keep ? cm_run : fmaxf(cm_run, cmx);
+            // while every score so far is masked, m_new = -inf: alpha 1, p = exp2(-inf) = 0
+            const float alpha = cm_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(cm_run - cm_new);
+            const float cm = cm_new == -INFINITY ? 0.f : cm_new;
             float psum = 0.f;
             static_for<0, 16>([&](auto r_c) __attribute__((always_inline)) {
                 constexpr int r = decltype(r_c)::value;
@@ -746,7 +766,7 @@ __global__ void __launch_bounds__(kThreads, 1) decode_kernel(const DecodeArgs a)
             // rescale O (lane l holds head l%32); skipped when no head's max rose.
             // O is zero until the first finite max, so it needs no rescale then.
             const uint32_t rose = (uint32_t)__builtin_amdgcn_ballot_w64(alpha != 1.f);
-            if (rose != 0 && __builtin_amdgcn_ballot_w64(m_run != -INFINITY) != 0) {
+            if (rose != 0 && __builtin_amdgcn_ballot_w64(cm_run != -INFINITY) != 0) {
 #pragma unroll
                 for (int dd = 0; dd < 8; ++dd)
 #pragma unroll
@@ -754,7 +774,7 @@ __global__ void __launch_bounds__(kThreads, 1) decode_kernel(const DecodeArgs a)
             }
             fill_soft(fc, IntC<7>{});
             l_run = l_run * alpha + psum;
-            m_run = m_new;
+            cm_run = cm_new;
 #pragma unroll
             for (int e = 0; e < 8; ++e) { p0[e] = (__bf16)s[e]; p1[e] = (__bf16)s[8 + e]; }
             fill_soft(fc, IntC<8>{});
@@ -829,25 +849,36 @@ __global__ void __launch_bounds__(kThreads, 1) decode_kernel(const DecodeArgs a)
 
         // ---- epilogue: both waves of a head block hold the same m, l ----
         // acc[d] register r, lane l: head 32-block base + l%32, dim 256 kh + 32 d +
-        // (r/4)*8 + 4*half + r%4 (four consecutive dims per register quad).
+        // (r/4)*8 + 4*(l/32) + r%4 (four consecutive dims per register quad).
+        // lane-dependent indices rebuilt from the lane id here, so that no
+        // 64-bit lane offset is kept live across the tile loop
+        const int ln_e = lane_id();
+        int wave_e = wave;
+        __asm__ volatile("" : "+s"(wave_e));       // wave-derived offsets rebuilt here too
+        const int kh_e = wave_e & 1, hb_e = wave_e >> 1;
+        const int H_e = MLA_LATE_ARG(DecodeArgs, h_q), sq_e = MLA_LATE_ARG(DecodeArgs, s_q);
+        const int head_e = hblk * kHeadsPerWG + hb_e * 32 + (ln_e & 31);
+        const int half_e = ln_e >> 5;
+        const bool head_ok_e = head_e < H_e;
         const bool final_out = (nsplit == 1);
-        const int b = j / a.s_q, iq = j - b * a.s_q;
-        if (final_out || (slot >= 0 && slot < a.max_slots)) {
+        const int b = j / sq_e, iq = j - b * sq_e;
+        if (final_out || (slot >= 0 && slot < MLA_LATE_ARG(DecodeArgs, max_slots))) {
             // l = 0: nothing visible (lse -inf, weight 0 in the merge); l NaN (a NaN
             // in q or the cache): lse NaN, so the merge propagates it
-            const float lse_v = l_run > 0.f ? (c * m_run + log2f(l_run)) * 0.69314718055994531f
+            const float lse_v = l_run > 0.f ? (cm_run + log2f(l_run)) * 0.69314718055994531f
                                              : (l_run == 0.f ? -INFINITY : __builtin_nanf(""));
             float inv = l_run > 0.f ? 1.f / l_run : 0.f;
             // attention sink: a final output is scaled by exp(lse) / (exp(lse) + exp(sink))
-            if (final_out && a.attn_sink && head_ok) inv *= 1.f / (1.f + __expf(a.attn_sink[head] - lse_v));
+            const float* attn_sink = MLA_LATE_ARG(DecodeArgs, attn_sink);
+            if (final_out && attn_sink && head_ok_e) inv *= 1.f / (1.f + __expf(attn_sink[head_e] - lse_v));
             // Split partials in float16 (when the output is bf16): each lane scales
             // its 128 values by 2^-E, E from the exponent of their largest
             // magnitude, so they lie in [-1, 1) and cannot overflow; E is stored
-            // in the head's exponent bytes 2 q + half of the dims d it holds
-            // (q = d / 128 in {2 kh, 2 kh + 1}, half = d % 8 / 4).
-            const bool part16 = !final_out && a.part_fp16;
+            // in the head's exponent bytes 2 q + h of the dims d it holds
+            // (q = d / 128 in {2 kh, 2 kh + 1}, h = d % 8 / 4, the lane's half).
+            const bool part16 = !final_out && MLA_LATE_ARG(DecodeArgs, part_fp16);
             int E = 0;
-            if (part16 && head_ok) {
+            if (part16 && head_ok_e) {
                 float amax = 0.f;
 #pragma unroll
                 for (int dd = 0; dd < 8; ++dd)
@@ -858,40 +889,40 @@ __global__ void __launch_bounds__(kThreads, 1) decode_kernel(const DecodeArgs a)
                 E = amax > 0.f ? (be == 0 ? -125 : be - 126) : 0;              // amax * 2^-E < 1
                 E = E > 127 ? 127 : E;
                 // the lane's dims span quarters 2 kh and 2 kh + 1 of the head
-                a.o_exp8[((int64_t)slot * H + head) * 8 + 4 * kh + half] = (unsigned char)(signed char)E;
-                a.o_exp8[((int64_t)slot * H + head) * 8 + 4 * kh + 2 + half] = (unsigned char)(signed char)E;
+                MLA_LATE_ARG(DecodeArgs, o_exp8)[((int64_t)slot * H_e + head_e) * 8 + 4 * kh_e + half_e] = (unsigned char)(signed char)E;
+                MLA_LATE_ARG(DecodeArgs, o_exp8)[((int64_t)slot * H_e + head_e) * 8 + 4 * kh_e + 2 + half_e] = (unsigned char)(signed char)E;
             }
-            if (head_ok) {
+            if (head_ok_e) {
 #pragma unroll
                 for (int dd = 0; dd < 8; ++dd) {
 #pragma unroll
                     for (int rq = 0; rq < 4; ++rq) {
-                        const int dim = 256 * kh + 32 * dd + 8 * rq + 4 * half;
+                        const int dim = 256 * kh_e + 32 * dd + 8 * rq + 4 * half_e;
                         const float v0 = acc[dd][4 * rq + 0] * inv, v1 = acc[dd][4 * rq + 1] * inv;
                         const float v2 = acc[dd][4 * rq + 2] * inv, v3 = acc[dd][4 * rq + 3] * inv;
                         if (part16) {
-                            const int64_t o = ((int64_t)slot * H + head) * kDv + dim;
+                            const int64_t o = ((int64_t)slot * H_e + head_e) * kDv + dim;
                             typedef __attribute__((__vector_size__(4 * sizeof(_Float16)))) _Float16 f16x4;
-                            *(f16x4*)((_Float16*)a.o_part + o) = f16x4{(_Float16)ldexpf(v0, -E), (_Float16)ldexpf(v1, -E),
+                            *(f16x4*)((_Float16*)MLA_LATE_ARG(DecodeArgs, o_part) + o) = f16x4{(_Float16)ldexpf(v0, -E), (_Float16)ldexpf(v1, -E),
                                                                          (_Float16)ldexpf(v2, -E), (_Float16)ldexpf(v3, -E)};
                         } else if (final_out) {
-                            const int64_t o = ((int64_t)j * H + head) * kDv + dim;
-                            if (a.out_fp32) {
-                                *(f32x4*)((float*)a.out + o) = f32x4{v0, v1, v2, v3};
+                            const int64_t o = ((int64_t)j * H_e + head_e) * kDv + dim;
+                            if (MLA_LATE_ARG(DecodeArgs, out_fp32)) {
+                                *(f32x4*)((float*)MLA_LATE_ARG(DecodeArgs, out) + o) = f32x4{v0, v1, v2, v3};
                             } else {
                                 const bf16x4 w = {(__bf16)v0, (__bf16)v1, (__bf16)v2, (__bf16)v3};
-                                *(bf16x4*)((__bf16*)a.out + o) = w;
+                                *(bf16x4*)((__bf16*)MLA_LATE_ARG(DecodeArgs, out) + o) = w;
                             }
                         } else {
-                            const int64_t o = ((int64_t)slot * H + head) * kDv + dim;
-                            *(f32x4*)(a.o_part + o) = f32x4{v0, v1, v2, v3};
+                            const int64_t o = ((int64_t)slot * H_e + head_e) * kDv + dim;
+                            *(f32x4*)(MLA_LATE_ARG(DecodeArgs, o_part) + o) = f32x4{v0, v1, v2, v3};
                         }
                     }
                 }
             }
-            if (kh == 0 && lane < 32 && head_ok) {
-                if (final_out) a.lse[((int64_t)b * H + head) * a.s_q + iq] = lse_v;
-                else a.lse_part[(int64_t)slot * H + head] = lse_v;
+            if (kh_e == 0 && ln_e < 32 && head_ok_e) {
+                if (final_out) MLA_LATE_ARG(DecodeArgs, lse)[((int64_t)b * H_e + head_e) * sq_e + iq] = lse_v;
+                else MLA_LATE_ARG(DecodeArgs, lse_part)[(int64_t)slot * H_e + head_e] = lse_v;
             }
         }
         lds_barrier();
@@ -906,8 +937,9 @@ hipError_t launch_decode(const DecodeArgs& a, bool sparse, int kvf, hipStream_t 
         else if (kvf == 1) hipLaunchKernelGGL((decode_kernel<true, 1>), grid, block, 0, stream, a);
         else hipLaunchKernelGGL((decode_kernel<true, 0>), grid, block, 0, stream, a);
     } else {
-        if (kvf == 1) hipLaunchKernelGGL((decode_kernel<false, 1>), grid, block, 0, stream, a);
-        else hipLaunchKernelGGL((decode_kernel<false, 0>), grid, block, 0, stream, a);
+        // the dense bf16 cache runs decode64_kernel
+        if (kvf != 1) return hipErrorInvalidValue;
+        hipLaunchKernelGGL((decode_kernel<false, 1>), grid, block, 0, stream, a);
     }
     return hipGetLastError();
 }

@@ -1,6 +1,6 @@
 """The build fails on register spills: the resource-report parser, the
-allowance ratchet, and a real gfx950 build (hipcc cross-compiles without a
-GPU) whose kernels are all within it."""
+allowance mechanism, and a real gfx950 build (hipcc cross-compiles without a
+GPU) in which no kernel spills or uses scratch memory."""
 
 import os
 
@@ -45,10 +45,9 @@ def test_real_build_has_no_unallowed_spills(tmp_path):
     assert os.path.exists(out)
     u = B.LAST_USAGE
     assert B.spill_problems(u) == []
-    # the dense bf16 kernel, the scheduler and the combine never spill
+    # every kernel of the library: no spills and no scratch
+    assert B.SPILL_ALLOWANCE == {}
     for name, r in u.items():
-        if "decode64_kernel" in name or "metadata_kernel" in name or "combine_kernel" in name:
-            assert r["ScratchSize [bytes/lane]"] == 0 and r["VGPRs Spill"] == 0 and r["SGPRs Spill"] == 0, name
-    assert any("decode64_kernel" in n for n in u)
-    # the allowance names only kernels that exist
-    assert set(B.SPILL_ALLOWANCE) <= set(u)
+        assert r["ScratchSize [bytes/lane]"] == 0 and r["VGPRs Spill"] == 0 and r["SGPRs Spill"] == 0, name
+    for k in ("decode64_kernel", "decode_kernel", "metadata_kernel", "combine_kernel"):
+        assert any(k in n for n in u), k
