@@ -288,6 +288,8 @@ def load_workload(name, dev):
 STEP_DENSE = ("mla_decode_step: schedule computed in the partial-attention kernel (batch * s_q <= 256, else "
               "the scheduler kernel first), partial attention, combine")
 STEP_SCHED = "mla_decode_step: scheduler kernel, partial attention, combine where an item is split"
+STEP_SPARSE = ("mla_decode_step: schedule computed in the partial-attention kernel (batch * s_q <= 256, else the "
+               "scheduler kernel first), partial attention, combine where an item is split")
 
 
 def describe(name, w):
@@ -312,7 +314,7 @@ def describe(name, w):
     if name == "config4":
         cfg = {"workload": "DSA top-k sparse decode b=64 s_q=1 h_q=128, top-k 2048 of a 32768-token pool per "
                            "request, 5% of slots -1, bf16 N(0,1)", "topk": w.topk, **base,
-               "step": STEP_SCHED}
+               "step": STEP_SPARSE}
         return "MLA sparse decode TFLOPS, µs/step at b=64,h_q=128,topk=2048 (1 GPU)", cfg, "hbm"
     if name == "config5":
         cfg = {"workload": "FP8 latent-cache decode b=32 s_q=1 h_q=128 seqlen=16384, 656-byte records (512 "
@@ -327,7 +329,7 @@ def describe(name, w):
     kind = "FP4" if w.kv_format == "fp4_288" else "FP8"
     cfg = {"workload": f"{kind} sparse absorbed-MLA decode b=128 s_q=2 h_q=128 top-k {topk} ({rec}, "
                        f"{max(32768, 2 * topk)} cached tokens per request, every slot valid, N(0,1) sources)",
-           "topk": topk, **base, "step": STEP_SCHED}
+           "topk": topk, **base, "step": STEP_SPARSE}
     return f"MLA sparse {kind} decode TFLOPS, µs/step at b=128,s_q=2,h_q=128,topk={topk}{tag} (1 GPU)", cfg, "mfma"
 
 
@@ -338,7 +340,9 @@ def kernel_name(w):
         return (f"decode64_kernel<{'true' if fused else 'false'}> (dense bf16 cache, 64 heads per workgroup"
                 + (", schedule computed in the kernel)" if fused else ")"))
     fmt = {"bf16": 0, "fp8": 1, "fp8_528": 2, "fp4_288": 3}[w.kv_format]
-    return f"decode_kernel<{'true' if w.topk else 'false'}, {fmt}> (128 heads per workgroup)"
+    fused = w.topk > 0 and w.batch * w.s_q <= 256
+    return (f"decode_kernel<{'true' if w.topk else 'false'}, {fmt}> (128 heads per workgroup"
+            + (", schedule computed in the kernel)" if fused else ")"))
 
 
 def bench_decode(args):

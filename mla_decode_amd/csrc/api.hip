@@ -130,10 +130,10 @@ bool sparse_items_whole(const mla_problem_t* p, const mla_metadata_t* m) {
     return q % cost == 0;
 }
 
-// Problems whose decode call computes its own schedule (decode64 kernel, up to
-// four items per lane of one wave).
+// Problems whose decode call computes its own schedule (up to four items per
+// lane of one wave): the dense bf16 kernel and the sparse kernels.
 bool step_fusable(const mla_problem_t* p) {
-    return uses_decode64(p) && (int64_t)p->batch * p->s_q <= mla::kMaxFusedItems;
+    return (uses_decode64(p) || p->topk > 0) && (int64_t)p->batch * p->s_q <= mla::kMaxFusedItems;
 }
 
 mla_status_t run_decode(const mla_problem_t* p, bool sparse, const void* q, const void* kv,
@@ -201,7 +201,8 @@ mla_status_t run_decode(const mla_problem_t* p, bool sparse, const void* q, cons
     const hipError_t e = uses_decode64(p) ? mla::launch_decode64(a, s) : mla::launch_decode(a, sparse, p->kv_format, s);
     if (e != hipSuccess) return MLA_ERR_HIP;
     if (fused && mla::debug_enabled()) {
-        st = mla::debug_check_call(p, meta, true, cache_seqlens, block_table, nullptr, num_rows, s, "mla_decode_step");
+        st = mla::debug_check_call(p, meta, true, cache_seqlens, sparse ? indices : block_table, topk_length, num_rows,
+                                   s, "mla_decode_step");
         if (st != MLA_OK) return st;
     }
 
@@ -401,8 +402,10 @@ mla_status_t mla_decode_step(const mla_problem_t* problem, const void* q, const 
     const bool sparse = problem->topk > 0;
     if (!table_or_indices || (!sparse && !cache_seqlens)) return MLA_ERR_INVALID_ARG;
     if (step_fusable(problem))
-        return run_decode(problem, false, q, kv_cache, table_or_indices, cache_seqlens, nullptr, nullptr, attn_sink,
-                          meta, workspace, workspace_bytes, out, lse, stream, true, 0, true, true);
+        return run_decode(problem, sparse, q, kv_cache, sparse ? nullptr : table_or_indices,
+                          sparse ? nullptr : cache_seqlens, sparse ? table_or_indices : nullptr,
+                          sparse ? topk_length : nullptr, attn_sink, meta, workspace, workspace_bytes, out, lse,
+                          stream, true, 0, true, true);
     st = mla_get_decode_metadata(problem, sparse ? nullptr : cache_seqlens, sparse ? topk_length : nullptr,
                                  (mla_metadata_t*)meta, stream);
     if (st != MLA_OK) return st;

@@ -39,6 +39,7 @@
 
 #include "common.h"
 #include "kernels.h"
+#include "wave_sched.h"
 
 namespace mla {
 
@@ -58,6 +59,7 @@ struct __attribute__((aligned(16))) Smem {
     bf16x8 qr[4][4][64];                    // RoPE part of Q as B fragments [head block][k-step][lane]
     int rows[4][kSubTok];                   // sparse: row ids of upcoming tiles (ring of 4)
     float f8scale[8][64];                   // FP8: per-wave scales of the tile being converted (lanes 32.. pad)
+    int seg_tab[kMaxFusedItems];            // fused schedule: item j's split count << 16 | first split slot
     unsigned char tile[kNBuf][kSubBytes];   // 32-token KV tiles (bf16, swizzled)
 };
 
@@ -383,9 +385,36 @@ __global__ void __launch_bounds__(kThreads, 1) decode_kernel(const DecodeArgs a)
     auto so_at = [&](int k) __attribute__((always_inline)) -> int {
         return sload(MLA_LATE_ARG(DecodeArgs, meta) + kMetaHeader + kMetaRec * MLA_LATE_ARG(DecodeArgs, num_parts) + k);
     };
-    const int jb = sload(rec + 0), tbeg = sload(rec + 1), je = sload(rec + 2), tend = sload(rec + 3);
-    const int slot0 = sload(rec + 4);
     const int N = a.batch * a.s_q;
+    // This partition's record: read from the scheduler's metadata, or (sparse
+    // calls with a.fused) computed by every wave from the top-k lengths with the
+    // scheduler's arithmetic.  Fused, wave 0 also writes the schedule back and
+    // keeps each item's split count and first split slot in LDS for the
+    // segments' epilogues.
+    const bool fused = SPARSE && a.fused;
+    int jb, tbeg, je, tend, slot0;
+    if (fused) {
+        const int ln = lane_id();
+        const int R = N <= 64 ? 1 : N <= 128 ? 2 : 4;
+        WaveSched ws;
+        wave_schedule_any(a, a.topk_length, N, part, ln, R, ws);
+        // uniform by construction; readfirstlane makes that visible to the compiler
+        jb = __builtin_amdgcn_readfirstlane(ws.jb);
+        tbeg = __builtin_amdgcn_readfirstlane(ws.tbeg);
+        je = __builtin_amdgcn_readfirstlane(ws.je);
+        tend = __builtin_amdgcn_readfirstlane(ws.tend);
+        slot0 = __builtin_amdgcn_readfirstlane(ws.slot0);
+        if (wave == 0) {
+            wave_schedule_store(a, N, part, ln, R, ws, hblk == 0, blockIdx.x == 0);
+            // entries past N (at most 64 * 4 = kMaxFusedItems in all) are never read
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+                if (u < R) sm.seg_tab[ln * R + u] = (ws.NS[u] << 16) | ws.SO[u];
+        }
+    } else {
+        jb = sload(rec + 0); tbeg = sload(rec + 1); je = sload(rec + 2); tend = sload(rec + 3);
+        slot0 = sload(rec + 4);
+    }
     const int H = a.h_q;
     const float c = a.scale_log2;
     const unsigned char* kv = (const unsigned char*)a.kv;
@@ -438,8 +467,6 @@ __global__ void __launch_bounds__(kThreads, 1) decode_kernel(const DecodeArgs a)
         int t1 = (j == je) ? tend : ntile_j;
         if (t1 > ntile_j) t1 = ntile_j;
         if (t0 >= t1) continue;
-        const int nsplit = so_at(j + 1) - so_at(j);
-        const int slot = (j == jb) ? slot0 : so_at(j);
         const int g0 = 2 * t0;                                    // first 32-token tile
         const int gend = min(2 * t1, (nslots + kSubTok - 1) / kSubTok);
         const int ns = gend - g0;
@@ -860,6 +887,17 @@ __global__ void __launch_bounds__(kThreads, 1) decode_kernel(const DecodeArgs a)
         const int head_e = hblk * kHeadsPerWG + hb_e * 32 + (ln_e & 31);
         const int half_e = ln_e >> 5;
         const bool head_ok_e = head_e < H_e;
+        // the item's split count and this partition's output slot (fused: the
+        // LDS table, written before the segment's first barrier)
+        int nsplit, slot;
+        if (fused) {
+            const int e = __builtin_amdgcn_readfirstlane(sm.seg_tab[j]);
+            nsplit = e >> 16;
+            slot = (j == jb) ? slot0 : (e & 0xffff);
+        } else {
+            nsplit = so_at(j + 1) - so_at(j);
+            slot = (j == jb) ? slot0 : so_at(j);
+        }
         const bool final_out = (nsplit == 1);
         const int b = j / sq_e, iq = j - b * sq_e;
         if (final_out || (slot >= 0 && slot < MLA_LATE_ARG(DecodeArgs, max_slots))) {

@@ -45,6 +45,7 @@
 
 #include "common.h"
 #include "kernels.h"
+#include "wave_sched.h"
 
 namespace mla {
 
@@ -160,110 +161,6 @@ __device__ __forceinline__ void unroll(F&& f) {
     }
 }
 
-// Inclusive prefix sum of one int per lane over the wave, in DPP moves (no
-// LDS): within rows of 16 lanes by shifts of 1, 2, 4 and 8, then the last
-// lane of row 0 into row 1 and of row 2 into row 3, then lane 31 into rows 2
-// and 3.  Lanes a move has no source for keep the identity 0.
-__device__ __forceinline__ int wave_scan_incl(int v) {
-    v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, false);   // row_shr:1
-    v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xf, 0xf, false);   // row_shr:2
-    v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xf, false);   // row_shr:4
-    v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xf, false);   // row_shr:8
-    v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xa, 0xf, false);   // row_bcast:15 into rows 1, 3
-    v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xc, 0xf, false);   // row_bcast:31 into rows 2, 3
-    return v;
-}
-
-// x / d for 0 <= x < 2^31 and 0 < d, given rd = 1 / d in double precision:
-// the estimate is within one of the quotient and is corrected once.
-__device__ __forceinline__ int div_rd(int x, int d, double rd) {
-    int y = (int)((double)x * rd);
-    y -= y * d > x ? 1 : 0;
-    y += (y + 1) * d <= x ? 1 : 0;
-    return y;
-}
-
-// The scheduler's arithmetic for partition ``part``, computed by one wave:
-// lane ln holds items ln * R + u (u < R) -- their tile counts Tl, the
-// exclusive prefix sum C of item cost (tiles + F), split counts NS and split
-// offsets SO -- and every lane gets the partition's record and the header
-// values T (total cost), q (cost per partition) and total (split slots).
-struct WaveSched {
-    int C[4], Tl[4], NS[4], SO[4];
-    int jb, tbeg, je, tend, slot0, T, q, total;
-};
-
-template <int R>
-__device__ __forceinline__ void wave_schedule(const DecodeArgs& a, int N, int part, int ln, WaveSched& w) {
-    const int F = a.fixed_overhead, P = a.num_parts;
-    const double rs = 1.0 / (double)a.s_q;
-    int own = 0;
-#pragma unroll
-    for (int u = 0; u < R; ++u) {
-        const int j = ln * R + u;
-        w.Tl[u] = 0;
-        if (j < N) {
-            const int b = div_rd(j, a.s_q, rs), i = j - b * a.s_q;
-            w.Tl[u] = (visible_len(clamp_len(a.cache_seqlens[b], a.max_blocks), a.s_q, i, a.causal) + 63) >> 6;
-            own += w.Tl[u] + F;
-        }
-    }
-    int incl = wave_scan_incl(own);
-    w.T = __builtin_amdgcn_readlane(incl, 63);
-    int run = incl - own;
-#pragma unroll
-    for (int u = 0; u < R; ++u) {
-        w.C[u] = run;
-        if (ln * R + u < N) run += w.Tl[u] + F;
-    }
-    w.q = w.T > 0 ? div_rd(w.T + P - 1, P, 1.0 / (double)P) : 1;
-    const double rq = 1.0 / (double)w.q;
-    own = 0;
-#pragma unroll
-    for (int u = 0; u < R; ++u) {
-        const int n = w.Tl[u], first = w.C[u] + F;
-        w.NS[u] = (ln * R + u < N && n > 0) ? div_rd(first + n - 1, w.q, rq) - div_rd(first, w.q, rq) + 1 : 0;
-        own += w.NS[u];
-    }
-    incl = wave_scan_incl(own);
-    w.total = __builtin_amdgcn_readlane(incl, 63);
-    run = incl - own;
-#pragma unroll
-    for (int u = 0; u < R; ++u) {
-        w.SO[u] = run;
-        run += w.NS[u];
-    }
-    // last item j with C[j] <= x: the C[j] are non-decreasing, so count them
-    auto item_of = [&](int x) __attribute__((always_inline)) -> int {
-        int cnt = 0;
-#pragma unroll
-        for (int u = 0; u < R; ++u) cnt += __builtin_popcountll(__builtin_amdgcn_ballot_w64(ln * R + u < N && w.C[u] <= x));
-        return cnt - 1;
-    };
-    auto at = [&](const int (&v)[4], int j) __attribute__((always_inline)) -> int {
-        const int u = j % R;
-        const int x = R == 1 ? v[0] : (u == 0 ? v[0] : u == 1 ? v[1] : u == 2 ? v[2] : v[3]);
-        return __builtin_amdgcn_readlane(x, j / R);
-    };
-    const int64_t lo64 = (int64_t)part * w.q;
-    const int64_t hi64 = lo64 + w.q < w.T ? lo64 + w.q : w.T;
-    if (lo64 >= hi64) {
-        w.jb = N; w.tbeg = 0; w.je = N; w.tend = 0; w.slot0 = 0;
-        return;
-    }
-    const int lo = (int)lo64, hi = (int)hi64;
-    w.jb = item_of(lo);
-    w.je = item_of(hi - 1);
-    const int Cjb = at(w.C, w.jb), njb = at(w.Tl, w.jb);
-    const int Cje = at(w.C, w.je), nje = at(w.Tl, w.je);
-    w.tbeg = lo - Cjb - F;
-    if (w.tbeg < 0) w.tbeg = 0;
-    w.tend = hi - Cje - F;
-    w.tend = w.tend < 0 ? 0 : (w.tend > nje ? nje : w.tend);
-    const int first_end = w.je == w.jb ? w.tend : njb;
-    w.slot0 = w.tbeg < first_end ? at(w.SO, w.jb) + part - div_rd(Cjb + F, w.q, rq) : 0;
-}
-
 }  // namespace
 
 template <bool FUSED>
@@ -309,32 +206,11 @@ __global__ void __launch_bounds__(kT, 1) decode64_kernel(const DecodeArgs a) {
     if constexpr (FUSED) {
         const int ln = (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
         fR = N <= 64 ? 1 : N <= 128 ? 2 : 4;
-        if (fR == 1) wave_schedule<1>(a, N, part, ln, ws);
-        else if (fR == 2) wave_schedule<2>(a, N, part, ln, ws);
-        else wave_schedule<4>(a, N, part, ln, ws);
+        wave_schedule_any(a, a.cache_seqlens, N, part, ln, fR, ws);
         jb = ws.jb; tbeg = ws.tbeg; je = ws.je; tend = ws.tend; slot0 = ws.slot0;
-        // the schedule written back in the scheduler's layout: each partition's
-        // record by its first head block, header and split offsets by
-        // workgroup 0 (copy wave 0 of each)
-        if (is_copy && cw == 0) {
-            int32_t* mo = a.meta_out;
-            if (hblk == 0 && ln == 0) {
-                int32_t* r = mo + kMetaHeader + kMetaRec * part;
-                r[0] = jb; r[1] = tbeg; r[2] = je; r[3] = tend; r[4] = slot0;
-            }
-            if (blockIdx.x == 0) {
-                int32_t* so_o = mo + kMetaHeader + kMetaRec * a.num_parts;
-#pragma unroll
-                for (int u = 0; u < 4; ++u)
-                    if (u < fR && ln * fR + u < N) so_o[ln * fR + u] = ws.SO[u];
-                if (ln == 0) {
-                    const int F = a.fixed_overhead;
-                    so_o[N] = ws.total;
-                    mo[0] = kMetaMagic; mo[1] = a.num_parts; mo[2] = N; mo[3] = F;
-                    mo[4] = ws.q; mo[5] = ws.T; mo[6] = a.s_q; mo[7] = ws.T - N * F;
-                }
-            }
-        }
+        // the schedule written back: each partition's record by its first head
+        // block, header and split offsets by workgroup 0 (copy wave 0 of each)
+        if (is_copy && cw == 0) wave_schedule_store(a, N, part, ln, fR, ws, hblk == 0, blockIdx.x == 0);
     } else {
         jb = sload(rec + 0), tbeg = sload(rec + 1), je = sload(rec + 2), tend = sload(rec + 3);
         slot0 = sload(rec + 4);

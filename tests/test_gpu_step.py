@@ -1,17 +1,19 @@
-"""The one-call decode step (mla_decode_step).  For dense bf16 problems of up
-to 256 query tokens the schedule is computed inside the partial-attention
-kernel; the metadata buffer it leaves must hold word for word what the
-scheduler kernel writes for the same lengths, and out/lse must equal, bit for
-bit, those of the metadata call followed by the decode call.  The cases cover
-one, two and four items per lane of the in-kernel scan, empty and one-token
-requests, partitions spanning many short requests, three head blocks, and a
-batch past the fused limit (scheduler kernel first)."""
+"""The one-call decode step (mla_decode_step).  For dense bf16 and top-k
+sparse problems of up to 256 query tokens the schedule is computed inside the
+partial-attention kernel; the metadata buffer it leaves must hold word for
+word what the scheduler kernel writes for the same lengths, and out/lse must
+equal, bit for bit, those of the metadata call followed by the decode call.
+The cases cover one, two and four items per lane of the in-kernel scan, empty
+and one-token requests, partitions spanning many short requests, three head
+blocks, sparse calls with and without per-token top-k lengths and with FP8 and
+FP4 records, the FP8 dense cache (scheduler kernel first) and a batch past the
+fused limit."""
 
 import numpy as np
 import pytest
 import torch
 
-from workloads import make_dense
+from workloads import make_dense, make_sparse, make_fp8_dense, make_fp4_sparse
 
 pytestmark = pytest.mark.gpu
 
@@ -40,7 +42,29 @@ CASES = {
     "b200_short": lambda: make_dense(200, 1, 64, _lens(200, 0, 130, 6), seed=6, device=DEV),
     "b3_h192_causal": lambda: make_dense(3, 2, 192, [1, 300, 777], causal=True, seed=7, device=DEV),
     "b300_not_fused": lambda: make_dense(300, 1, 32, _lens(300, 1, 200, 8), seed=8, device=DEV),
+    "sparse_b64": lambda: make_sparse(64, 1, 128, pool_tokens_per_seq=512, topk=200, invalid_frac=0.05, seed=10,
+                                      device=DEV),
+    "sparse_b128_s2_fp8": lambda: make_sparse(128, 2, 64, pool_tokens_per_seq=256, topk=128, seed=11, device=DEV,
+                                              kv_format="fp8"),
+    "sparse_b3_fp4": lambda: make_fp4_sparse(3, 2, 128, pool_tokens_per_seq=1024, topk=333, invalid_frac=0.1,
+                                             seed=12, device=DEV),
+    "sparse_b150_not_fused": lambda: make_sparse(150, 2, 16, pool_tokens_per_seq=128, topk=64, seed=13,
+                                                 device=DEV),
+    "fp8_dense_b4": lambda: make_fp8_dense(4, 1, 128, [1, 500, 1000, 64], seed=14, device=DEV),
 }
+
+
+def _with_topk_length(w, seed):
+    """A copy of sparse workload w with per-token top-k lengths in [0, topk], some 0."""
+    g = torch.Generator(device="cpu").manual_seed(seed)
+    tl = torch.randint(0, w.topk + 1, (w.batch, w.s_q), generator=g, dtype=torch.int32)
+    tl.view(-1)[::7] = 0
+    w.topk_length = tl.to(DEV)
+    return w
+
+
+CASES["sparse_b64_topk_length"] = lambda: _with_topk_length(
+    make_sparse(64, 2, 128, pool_tokens_per_seq=512, topk=300, seed=15, device=DEV), 16)
 
 
 @pytest.mark.parametrize("name", list(CASES))
@@ -50,22 +74,25 @@ def test_step_matches_metadata_then_decode(name):
     w = CASES[name]()
     dec = mla.Decoder.for_workload(w, DEV)
     words = dec.meta.bytes // 4
-    dec.metadata(w.cache_seqlens)
+    tl = getattr(w, "topk_length", None)
+    sl = None if w.topk else w.cache_seqlens
+    dec.metadata(sl, topk_length=tl)
     ref_meta = dec.meta_buf.view(torch.int32)[:words].clone()
-    o1, l1 = dec.decode(w.q, w.kv, w.block_table, w.cache_seqlens)
+    o1, l1 = dec.decode(w.q, w.kv, w.block_table, w.cache_seqlens, w.indices, topk_length=tl)
     o1, l1 = o1.clone(), l1.clone()
     dec.meta_buf.fill_(-7)
     dec.out.fill_(float("nan"))
     dec.lse.fill_(float("nan"))
-    o2, l2 = dec.step(w.q, w.kv, w.block_table, w.cache_seqlens)
+    o2, l2 = dec.step(w.q, w.kv, w.block_table, sl, w.indices, topk_length=tl)
     torch.cuda.synchronize()
     got_meta = dec.meta_buf.view(torch.int32)[:words]
     assert torch.equal(got_meta, ref_meta), (got_meta - ref_meta).nonzero()[:8].tolist()
-    assert torch.equal(o1, o2)
-    assert torch.equal(l1, l2)
+    assert torch.equal(o1.view(torch.int16 if o1.dtype == torch.bfloat16 else torch.int32),
+                       o2.view(torch.int16 if o2.dtype == torch.bfloat16 else torch.int32))
+    assert torch.equal(l1.view(torch.int32), l2.view(torch.int32))
     # the schedule left behind serves a later decode call with the same lengths
-    o3, l3 = dec.decode(w.q, w.kv, w.block_table, w.cache_seqlens)
-    assert torch.equal(o1, o3) and torch.equal(l1, l3)
+    o3, l3 = dec.decode(w.q, w.kv, w.block_table, w.cache_seqlens, w.indices, topk_length=tl)
+    assert torch.equal(o1, o3) and torch.equal(l1.view(torch.int32), l3.view(torch.int32))
 
 
 def test_step_follows_new_lengths():
