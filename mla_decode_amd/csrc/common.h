@@ -130,6 +130,15 @@ struct RowResolver {
     }
 };
 
+// max(a, b, c) as one v_max3_f32.  Written as assembly because the compiler
+// would first quiet signalling NaNs in every input with an extra max(x, x);
+// scores out of MFMAs hold no signalling NaN.
+__device__ __forceinline__ float max3_raw(float a, float b, float c) {
+    float r;
+    __asm__("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+    return r;
+}
+
 __device__ __forceinline__ float wave_max_pair(float x) {
     // lanes l and l^32 hold one head's two halves; after the swap both lanes
     // see both values

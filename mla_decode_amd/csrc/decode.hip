@@ -765,10 +765,15 @@ __global__ void __launch_bounds__(kThreads, 1) decode_kernel(const DecodeArgs a)
                     if (!valid) s[r] = -INFINITY;
                 }
             }
-            float mx = -INFINITY;
-#pragma unroll
-            for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[r]);
-            mx = wave_max_pair(mx);
+            // tile max in v_max3 (the scores hold no signalling NaN, so no
+            // quieting max(x, x) per input), then across the lane pair
+            float mx = max3_raw(max3_raw(s[0], s[1], s[2]), max3_raw(s[3], s[4], s[5]), max3_raw(s[6], s[7], s[8]));
+            mx = max3_raw(mx, max3_raw(s[9], s[10], s[11]), max3_raw(s[12], s[13], s[14]));
+            mx = max3_raw(mx, s[15], s[15]);
+            {
+                auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+                mx = max3_raw(__uint_as_float(r[0]), __uint_as_float(r[1]), __uint_as_float(r[1]));
+            }
             fill_soft(fc, IntC<2>{});
             fill_soft(fc, IntC<3>{});
             // Running max: raised to the tile max only when that exceeds it by

@@ -406,11 +406,14 @@ __global__ void __launch_bounds__(kT, 1) decode64_kernel(const DecodeArgs a) {
             auto soft_stage = [&](auto st_c, int tslot) __attribute__((always_inline)) {
                 constexpr int st = decltype(st_c)::value;
                 if constexpr (st == 0) {
-                    mxa = fmaxf(fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3])), fmaxf(fmaxf(s[4], s[5]), fmaxf(s[6], s[7])));
+                    mxa = max3_raw(max3_raw(s[0], s[1], s[2]), max3_raw(s[3], s[4], s[5]), max3_raw(s[6], s[7], s[7]));
                 } else if constexpr (st == 1) {
-                    mxb = fmaxf(fmaxf(fmaxf(s[8], s[9]), fmaxf(s[10], s[11])), fmaxf(fmaxf(s[12], s[13]), fmaxf(s[14], s[15])));
+                    mxb = max3_raw(max3_raw(s[8], s[9], s[10]), max3_raw(s[11], s[12], s[13]), max3_raw(s[14], s[15], s[15]));
                 } else if constexpr (st == 2) {
-                    mxa = wave_max_pair(fmaxf(mxa, mxb));   // the two lanes of a head hold disjoint tokens
+                    // the two lanes of a head hold disjoint tokens
+                    const float m2 = max3_raw(mxa, mxb, mxb);
+                    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(m2), __float_as_uint(m2), false, false);
+                    mxa = max3_raw(__uint_as_float(r[0]), __uint_as_float(r[1]), __uint_as_float(r[1]));
                 } else if constexpr (st == 3) {
                     const bool keep = c * (mxa - m_run) <= a.rescale_tau;
                     m_new = keep ? m_run : fmaxf(m_run, mxa);
