@@ -274,8 +274,8 @@ mla_status_t mla_debug_gather_rows(const mla_problem_t *problem, const int32_t *
  * current lengths, the partial-attention kernel and the combine.  The pages'
  * newer interface makes the metadata call a placeholder and lets the first
  * decode call compute the schedule on the device and keep it for the layers
- * and steps that follow (FlashMLA deep dive, "tile_scheduler_metadata";
- * sparse decoding usage note); this call does the same every time it runs and
+ * and steps that follow (the "matrices, attention & GPU" explainer, split-KV
+ * section; FlashMLA README, "Usage", DSA decoding); this call does the same every time it runs and
  * writes the schedule to meta->dev, so later mla_decode_fwd /
  * mla_sparse_decode_fwd calls with the same lengths can reuse ``meta``.
  * Dense bf16 and top-k sparse problems with batch * s_q <= 256 compute the
