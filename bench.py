@@ -393,7 +393,6 @@ def bench_decode(args):
         lambda: dec.decode_partial(w.q, w.kv, w.block_table, w.cache_seqlens, w.indices, stream, production=True,
                                    fused=True),
         args.steps, stream, before)
-    ms_meta, _ = _timed(lambda: dec.metadata(seqlens, stream), args.steps, stream)
 
     flops, nbytes, kbytes = acct["flops"], acct["bytes"], acct["partial_bytes"]
     tflops = flops / (ms_step * 1e-3) / 1e12
@@ -434,7 +433,6 @@ def bench_decode(args):
         "roofline": roofline,
         "roofline_other": {"bound": "mfma" if bound == "hbm" else "hbm", **other},
         "decode_call_us": round(ms_decode * 1e3, 2),
-        "metadata_us": round(ms_meta * 1e3, 2),
     }
     del graph
     if scratch is not None:
