@@ -395,14 +395,17 @@ __global__ void __launch_bounds__(kT, 1) decode64_kernel(const DecodeArgs a) {
             barrier_lds();   // tile 0 has landed
 
             // Softmax of the tile whose scores are in s, in stages that run
-            // between the MFMAs of the next tile's QK (stage st after MFMA st):
+            // between the MFMAs of the next tile's QK (stage st after MFMA st +
+            // kSoftOffset, so that the step's first MFMAs issue back to back
+            // while their K fragments arrive):
             // tile max, the exact running max (raised when the tile max exceeds
             // it by more than tau in log2 units; tau = 0: whenever it is
             // larger), alpha, p = exp2(s c - m c) one score per stage, l, then
             // P rounded to bf16 and published with alpha.
             float mxa = 0.f, mxb = 0.f, m_new = 0.f, cm = 0.f, alpha = 0.f, psum = 0.f;
             bf16x8 p0 = {}, p1 = {};
-            constexpr int kSoftStages = 27;
+            constexpr int kSoftStages = 27, kSoftOffset = 3;
+            static_assert(kSoftStages + kSoftOffset <= 36, "every softmax stage follows a QK MFMA");
             auto soft_stage = [&](auto st_c, int tslot) __attribute__((always_inline)) {
                 constexpr int st = decltype(st_c)::value;
                 if constexpr (st == 0) {
@@ -450,7 +453,7 @@ __global__ void __launch_bounds__(kT, 1) decode64_kernel(const DecodeArgs a) {
             // QK(t): S^T = K Q^T over 36 k-steps, even k-steps into sa and odd
             // ones into sb, K fragments read kQkLA ahead.  The order is fixed
             // with scheduling fences: MFMA i, the read of fragment i + kQkLA,
-            // then softmax stage i of the previous tile when SOFT.
+            // then softmax stage i - kSoftOffset of the previous tile when SOFT.
             auto qk = [&](int t, auto soft_c, int tslot, auto&& pre) __attribute__((always_inline)) {
                 constexpr bool SOFT = decltype(soft_c)::value != 0;
                 // K operand of k-step kk: token l % 32, column 2 kk + half; its
@@ -478,7 +481,8 @@ __global__ void __launch_bounds__(kT, 1) decode64_kernel(const DecodeArgs a) {
                     else sa = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, qf[i], sa, 0, 0, 0);
                     if constexpr (i + kQkLA < 36)
                         fr[(i + kQkLA) % (kQkLA + 1)] = *(const bf16x8*)(T + 4096 * ((i + kQkLA) >> 2) + kb[(i + kQkLA) & 3]);
-                    if constexpr (SOFT && i < kSoftStages) soft_stage(Int<i>{}, tslot);
+                    if constexpr (SOFT && i >= kSoftOffset && i - kSoftOffset < kSoftStages)
+                        soft_stage(Int<i - kSoftOffset>{}, tslot);
                     __builtin_amdgcn_sched_barrier(0);
                 });
             };
