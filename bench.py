@@ -287,7 +287,6 @@ def load_workload(name, dev):
 
 STEP_DENSE = ("mla_decode_step: schedule computed in the partial-attention kernel (batch * s_q <= 256, else "
               "the scheduler kernel first), partial attention, combine")
-STEP_SCHED = "mla_decode_step: scheduler kernel, partial attention, combine where an item is split"
 STEP_SPARSE = ("mla_decode_step: schedule computed in the partial-attention kernel (batch * s_q <= 256, else the "
                "scheduler kernel first), partial attention, combine where an item is split")
 
@@ -319,7 +318,7 @@ def describe(name, w):
     if name == "config5":
         cfg = {"workload": "FP8 latent-cache decode b=32 s_q=1 h_q=128 seqlen=16384, 656-byte records (512 "
                            "e4m3 + 4 fp32 scales + 64 bf16 RoPE), q bf16 N(0,1)", "seqlen": 16384, **base,
-               "step": STEP_SCHED}
+               "step": STEP_SPARSE}
         return "MLA FP8-cache decode TFLOPS, µs/step at b=32,h_q=128,seqlen=16384 (1 GPU)", cfg, "mfma"
     topk = w.topk
     rec = {"fp8_528": "528-byte records of the 512-wide head (e8m0 scales per 32 values)",
@@ -340,8 +339,10 @@ def kernel_name(w):
         return (f"decode64_kernel<{'true' if fused else 'false'}> (dense bf16 cache, 64 heads per workgroup"
                 + (", schedule computed in the kernel)" if fused else ")"))
     fmt = {"bf16": 0, "fp8": 1, "fp8_528": 2, "fp4_288": 3}[w.kv_format]
-    fused = w.topk > 0 and w.batch * w.s_q <= 256
-    return (f"decode_kernel<{'true' if w.topk else 'false'}, {fmt}> (128 heads per workgroup"
+    fused = w.batch * w.s_q <= 256
+    # the third argument selects the dense instantiation that computes its own schedule
+    dense_fused = "true" if not w.topk and fused else "false"
+    return (f"decode_kernel<{'true' if w.topk else 'false'}, {fmt}, {dense_fused}> (128 heads per workgroup"
             + (", schedule computed in the kernel)" if fused else ")"))
 
 

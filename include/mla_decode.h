@@ -247,8 +247,8 @@ mla_status_t mla_combine(int32_t num_items, int32_t h_q, int32_t s_q, const floa
  * per lane by a power of two when the output is bf16, float32 otherwise), so
  * that the launch is the one mla_decode_fwd makes.  partial_format 2: the
  * launch mla_decode_step makes -- format 1, with the schedule computed inside
- * the kernel and written to meta->dev where mla_decode_step does that (dense
- * bf16 or top-k sparse, batch * s_q <= 256), format 1 otherwise.  ``table_or_indices`` is
+ * the kernel and written to meta->dev where mla_decode_step does that
+ * (batch * s_q <= 256), format 1 otherwise.  ``table_or_indices`` is
  * block_table (dense) or indices (sparse); cache_seqlens is ignored for sparse
  * problems, topk_length for dense ones; attn_sink applies to the outputs this
  * call writes.  Same errors as mla_decode_fwd, plus INVALID_ARG for another
@@ -278,10 +278,9 @@ mla_status_t mla_debug_gather_rows(const mla_problem_t *problem, const int32_t *
  * section; FlashMLA README, "Usage", DSA decoding); this call does the same every time it runs and
  * writes the schedule to meta->dev, so later mla_decode_fwd /
  * mla_sparse_decode_fwd calls with the same lengths can reuse ``meta``.
- * Dense bf16 and top-k sparse problems with batch * s_q <= 256 compute the
- * schedule inside the partial-attention kernel (no scheduler launch); every
- * other problem (the FP8 dense cache, larger batches) runs
- * mla_get_decode_metadata first.  Either way meta->dev ends up holding the
+ * Problems with batch * s_q <= 256 (every cache format, dense or sparse)
+ * compute the schedule inside the partial-attention kernel (no scheduler
+ * launch); larger batches run mla_get_decode_metadata first.  Either way meta->dev ends up holding the
  * words mla_get_decode_metadata would write, and out/lse are bit-identical to
  * that call followed by the decode call.  Arguments as for those calls:
  * table_or_indices is block_table (dense, with cache_seqlens) or indices

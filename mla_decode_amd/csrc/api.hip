@@ -131,9 +131,9 @@ bool sparse_items_whole(const mla_problem_t* p, const mla_metadata_t* m) {
 }
 
 // Problems whose decode call computes its own schedule (up to four items per
-// lane of one wave): the dense bf16 kernel and the sparse kernels.
+// lane of one wave): every cache format, dense or sparse.
 bool step_fusable(const mla_problem_t* p) {
-    return (uses_decode64(p) || p->topk > 0) && (int64_t)p->batch * p->s_q <= mla::kMaxFusedItems;
+    return (int64_t)p->batch * p->s_q <= mla::kMaxFusedItems;
 }
 
 mla_status_t run_decode(const mla_problem_t* p, bool sparse, const void* q, const void* kv,

@@ -342,8 +342,11 @@ struct FillCtx {
 };
 
 // KVF: cache format, 0 = bf16 rows of 576, 1 = 656-byte FP8 records, 2 =
-// 528-byte FP8 records of the 512-wide head (K = V = all 512 dims, no RoPE part)
-template <bool SPARSE, int KVF>
+// 528-byte FP8 records of the 512-wide head (K = V = all 512 dims, no RoPE part).
+// DFUSED (dense calls): the schedule is computed in the kernel; a separate
+// instantiation, so that the dense kernel that reads the metadata carries no
+// code of the other path.  Sparse calls choose at run time (a.fused).
+template <bool SPARSE, int KVF, bool DFUSED = false>
 __global__ void __launch_bounds__(kThreads, 1) decode_kernel(const DecodeArgs a) {
     constexpr bool FP8 = KVF != 0;                            // quantised cache (copied raw, dequantised in LDS)
     constexpr bool FP4 = KVF == 3;
@@ -386,18 +389,18 @@ __global__ void __launch_bounds__(kThreads, 1) decode_kernel(const DecodeArgs a)
         return sload(MLA_LATE_ARG(DecodeArgs, meta) + kMetaHeader + kMetaRec * MLA_LATE_ARG(DecodeArgs, num_parts) + k);
     };
     const int N = a.batch * a.s_q;
-    // This partition's record: read from the scheduler's metadata, or (sparse
-    // calls with a.fused) computed by every wave from the top-k lengths with the
-    // scheduler's arithmetic.  Fused, wave 0 also writes the schedule back and
-    // keeps each item's split count and first split slot in LDS for the
-    // segments' epilogues.
-    const bool fused = SPARSE && a.fused;
+    // This partition's record: read from the scheduler's metadata, or (fused)
+    // computed by every wave from the lengths (top-k lengths, or the cache
+    // lengths of a dense call) with the scheduler's arithmetic.  Fused, wave 0
+    // also writes the schedule back and keeps each item's split count and first
+    // split slot in LDS for the segments' epilogues.
+    const bool fused = SPARSE ? a.fused != 0 : DFUSED;
     int jb, tbeg, je, tend, slot0;
     if (fused) {
         const int ln = lane_id();
         const int R = N <= 64 ? 1 : N <= 128 ? 2 : 4;
         WaveSched ws;
-        wave_schedule_any(a, a.topk_length, N, part, ln, R, ws);
+        wave_schedule_any(a, SPARSE ? a.topk_length : a.cache_seqlens, N, part, ln, R, ws);
         // uniform by construction; readfirstlane makes that visible to the compiler
         jb = __builtin_amdgcn_readfirstlane(ws.jb);
         tbeg = __builtin_amdgcn_readfirstlane(ws.tbeg);
@@ -982,7 +985,8 @@ hipError_t launch_decode(const DecodeArgs& a, bool sparse, int kvf, hipStream_t 
     } else {
         // the dense bf16 cache runs decode64_kernel
         if (kvf != 1) return hipErrorInvalidValue;
-        hipLaunchKernelGGL((decode_kernel<false, 1>), grid, block, 0, stream, a);
+        if (a.fused) hipLaunchKernelGGL((decode_kernel<false, 1, true>), grid, block, 0, stream, a);
+        else hipLaunchKernelGGL((decode_kernel<false, 1>), grid, block, 0, stream, a);
     }
     return hipGetLastError();
 }

@@ -51,6 +51,9 @@ CASES = {
     "sparse_b150_not_fused": lambda: make_sparse(150, 2, 16, pool_tokens_per_seq=128, topk=64, seed=13,
                                                  device=DEV),
     "fp8_dense_b4": lambda: make_fp8_dense(4, 1, 128, [1, 500, 1000, 64], seed=14, device=DEV),
+    "fp8_dense_b70_s2_causal": lambda: make_fp8_dense(70, 2, 128, _lens(70, 1, 900, 17), causal=True, seed=17,
+                                                      device=DEV),
+    "fp8_dense_b300_not_fused": lambda: make_fp8_dense(300, 1, 16, _lens(300, 1, 200, 18), seed=18, device=DEV),
 }
 
 
