@@ -295,8 +295,8 @@ def debug_decode_partial(problem, q, kv_cache, table_or_indices, cache_seqlens, 
 def decode_step(problem, q, kv_cache, table_or_indices, meta, meta_buf, workspace, out, lse, cache_seqlens=None,
                 topk_length=None, attn_sink=None, stream=None):
     """A whole decode step in one call (mla_decode_step): the schedule for the current lengths, written to
-    ``meta_buf`` as the metadata call would, then the decode.  Dense bf16 and top-k sparse problems with
-    batch * s_q <= 256 compute the schedule inside the partial-attention kernel."""
+    ``meta_buf`` as the metadata call would, then the decode.  Problems with batch * s_q <= 256 (every cache
+    format) compute the schedule inside the partial-attention kernel."""
     lib = _lib.load()
     _check_q_out(problem, q, out, lse)
     _check_kv(problem, kv_cache, problem.num_blocks * 64)

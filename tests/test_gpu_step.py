@@ -1,13 +1,13 @@
-"""The one-call decode step (mla_decode_step).  For dense bf16 and top-k
-sparse problems of up to 256 query tokens the schedule is computed inside the
+"""The one-call decode step (mla_decode_step).  For problems of up to 256
+query tokens (every cache format) the schedule is computed inside the
 partial-attention kernel; the metadata buffer it leaves must hold word for
 word what the scheduler kernel writes for the same lengths, and out/lse must
 equal, bit for bit, those of the metadata call followed by the decode call.
 The cases cover one, two and four items per lane of the in-kernel scan, empty
 and one-token requests, partitions spanning many short requests, three head
 blocks, sparse calls with and without per-token top-k lengths and with FP8 and
-FP4 records, the FP8 dense cache (scheduler kernel first) and a batch past the
-fused limit."""
+FP4 records, the FP8 dense cache (causal, ragged) and batches past the fused
+limit (scheduler kernel first)."""
 
 import numpy as np
 import pytest
