@@ -914,9 +914,11 @@ __global__ void __launch_bounds__(kThreads, 1) decode_kernel(const DecodeArgs a)
             const float lse_v = l_run > 0.f ? (cm_run + log2f(l_run)) * 0.69314718055994531f
                                              : (l_run == 0.f ? -INFINITY : __builtin_nanf(""));
             float inv = l_run > 0.f ? 1.f / l_run : 0.f;
-            // attention sink: a final output is scaled by exp(lse) / (exp(lse) + exp(sink))
+            // attention sink: a final output is scaled by exp(lse) / (exp(lse) + exp(sink));
+            // a row that saw nothing stays 0 (with lse = sink = -inf the factor would be NaN)
             const float* attn_sink = MLA_LATE_ARG(DecodeArgs, attn_sink);
-            if (final_out && attn_sink && head_ok_e) inv *= 1.f / (1.f + __expf(attn_sink[head_e] - lse_v));
+            if (final_out && attn_sink && head_ok_e && l_run > 0.f)
+                inv *= 1.f / (1.f + __expf(attn_sink[head_e] - lse_v));
             // Split partials in float16 (when the output is bf16): each lane scales
             // its 128 values by 2^-E, E from the exponent of their largest
             // magnitude, so they lie in [-1, 1) and cannot overflow; E is stored

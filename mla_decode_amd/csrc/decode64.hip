@@ -525,7 +525,10 @@ __global__ void __launch_bounds__(kT, 1) decode64_kernel(const DecodeArgs a) {
                 const float lse_v = l_run > 0.f ? (c * m_run + log2f(l_run)) * 0.69314718055994531f
                                                  : (l_run == 0.f ? -INFINITY : __builtin_nanf(""));
                 float inv = l_run > 0.f ? 1.f / l_run : 0.f;
-                if (sg.final_out && a.attn_sink && hd < H) inv *= 1.f / (1.f + __expf(a.attn_sink[hd] - lse_v));
+                // attention sink on a final output; a row that saw nothing stays 0
+                // (with lse = sink = -inf the factor would be NaN)
+                if (sg.final_out && a.attn_sink && hd < H && l_run > 0.f)
+                    inv *= 1.f / (1.f + __expf(a.attn_sink[hd] - lse_v));
                 sm.fin_inv[hbq * 32 + (l & 31)] = inv;
                 if (l < 32 && hd < H && sg.write_ok) {
                     if (sg.final_out) a.lse[((int64_t)sg.b * H + hd) * a.s_q + sg.iq] = lse_v;

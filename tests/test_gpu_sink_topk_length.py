@@ -96,6 +96,27 @@ def test_sparse_topk_length_and_sink(kv_format):
         _say(num_cus, compare(go, gl, ro, rl, **kw))
 
 
+@pytest.mark.parametrize("num_cus", [12, 48])
+def test_sparse_rows_seeing_nothing_with_sink(num_cus):
+    """Rows whose top-k entries are all -1 see nothing: out stays 0 and lse is
+    -inf with a sink too, also for a head whose sink is -inf (where the sink
+    factor exp(lse) / (exp(lse) + exp(sink)) itself would be 0 / 0).  The 12
+    items have four 64-token tiles each: with 12 partitions every item is
+    whole (the decode kernel writes the output), with 48 every tile is a
+    split (the combine does)."""
+    _say(f"sparse rows seeing nothing, sink, num_cus={num_cus}")
+    w = make_sparse(6, 2, 128, pool_tokens_per_seq=256, topk=200, seed=43, device=DEV)
+    w.indices[0, 0, :] = -1
+    w.indices[3, 1, :] = -1
+    w.indices[5, :, :] = -1
+    w.attn_sink = _sink(128, 4)
+    go, gl, _ = run_library(w, num_cus=num_cus)
+    ro, rl = oracle(w)
+    for b, i in ((0, 0), (3, 1), (5, 0), (5, 1)):
+        assert np.all(go[b, i] == 0.0) and np.all(np.isneginf(gl[b, :, i]))
+    _say(compare(go, gl, ro, rl))
+
+
 def test_gather_rows_with_topk_length():
     import mla_decode_amd as mla
     w = make_sparse(3, 2, 16, pool_tokens_per_seq=512, topk=100, invalid_frac=0.2, seed=44, device=DEV)
