@@ -96,3 +96,49 @@ def compare(got_out, got_lse, ref_out, ref_lse, items=None, rel_l2=OUT_REL_L2, m
     if empty.any():
         assert np.all(go[empty] == 0.0)
     return stats
+
+
+RANDOM_KINDS = ("dense", "fp8", "sparse", "sparse_fp8", "v41", "fp4")
+RANDOM_EDGE = (0, 1, 63, 64, 65, 128)
+
+
+def draw_random_problem(seed, device):
+    """A seeded random decode problem: (cache format, workload, description).
+    The format cycles over RANDOM_KINDS; batch, s_q, heads, lengths or top-k
+    sizes (mixed with the edge values 0, 1, 63, 64, 65, 128), causal masking,
+    output type, sink and per-query top-k lengths are drawn."""
+    from workloads import make_dense, make_sparse, make_fp8_dense, make_v41_sparse, make_fp4_sparse
+    DEV = device
+    r = np.random.default_rng(5000 + seed)
+    kind = RANDOM_KINDS[seed % len(RANDOM_KINDS)]
+    B = int(r.integers(1, 25))
+    S = int(r.choice([1, 1, 2, 3]))
+    H = int(r.choice([16, 40, 64, 100, 128, 192]))
+    out_dtype = str(r.choice(["bf16", "fp32"]))
+    if kind in ("dense", "fp8"):
+        lens = [int(x) if r.random() < 0.7 else int(r.choice(RANDOM_EDGE)) for x in r.integers(0, 1201, size=B)]
+        causal = bool(S > 1 and r.random() < 0.7)
+        make = make_dense if kind == "dense" else make_fp8_dense
+        w = make(B, S, H, lens, causal=causal, seed=seed, device=DEV, out_dtype=out_dtype)
+        desc = f"{kind} B={B} S={S} H={H} out={out_dtype} causal={causal} lens={lens[:6]}"
+    else:
+        pool = int(r.choice([256, 512, 1024]))
+        topk = int(r.choice(RANDOM_EDGE[1:]) if r.random() < 0.3 else r.integers(1, min(pool, 700) + 1))
+        inv = float(r.choice([0.0, 0.05, 0.2]))
+        if kind in ("sparse", "sparse_fp8"):
+            w = make_sparse(B, S, H, pool_tokens_per_seq=pool, topk=topk, invalid_frac=inv, seed=seed, device=DEV,
+                            out_dtype=out_dtype, kv_format="fp8" if kind == "sparse_fp8" else "bf16")
+        else:
+            make = make_v41_sparse if kind == "v41" else make_fp4_sparse
+            w = make(B, S, H, pool_tokens_per_seq=pool, topk=topk, invalid_frac=inv, seed=seed, device=DEV)
+            w.out_dtype = out_dtype
+        if r.random() < 0.4:
+            tl = torch.as_tensor(r.integers(0, topk + 1, size=(B, S)), dtype=torch.int32)
+            w.topk_length = tl.to(DEV)
+        desc = f"{kind} B={B} S={S} H={H} out={out_dtype} pool={pool} topk={topk} invalid={inv}"
+    if r.random() < 0.3:
+        s = torch.as_tensor(r.normal(8.0, 4.0, size=H), dtype=torch.float32)
+        s[0] = -float("inf")
+        w.attn_sink = s.to(DEV)
+        desc += " sink"
+    return kind, w, desc

@@ -18,14 +18,12 @@ import pytest
 import torch
 
 from oracle import attention as A
-from workloads import make_dense, make_sparse, make_fp8_dense, make_v41_sparse, make_fp4_sparse, make_sparse_prefill
-from helpers import oracle, compare, bits16, FP8_REL_L2
+from workloads import make_dense, make_sparse, make_fp8_dense, make_sparse_prefill
+from helpers import oracle, compare, bits16, draw_random_problem, FP8_REL_L2
 
 pytestmark = pytest.mark.gpu
 
 DEV = "cuda"
-KINDS = ("dense", "fp8", "sparse", "sparse_fp8", "v41", "fp4")
-EDGE = (0, 1, 63, 64, 65, 128)
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -34,43 +32,6 @@ def _gpu():
         pytest.skip("no GPU")
     import mla_decode_amd._lib as L
     L.load()   # fails loudly if the HIP library is missing
-
-
-def _draw(seed):
-    """The case of ``seed``: (workload, description)."""
-    r = np.random.default_rng(5000 + seed)
-    kind = KINDS[seed % len(KINDS)]
-    B = int(r.integers(1, 25))
-    S = int(r.choice([1, 1, 2, 3]))
-    H = int(r.choice([16, 40, 64, 100, 128, 192]))
-    out_dtype = str(r.choice(["bf16", "fp32"]))
-    if kind in ("dense", "fp8"):
-        lens = [int(x) if r.random() < 0.7 else int(r.choice(EDGE)) for x in r.integers(0, 1201, size=B)]
-        causal = bool(S > 1 and r.random() < 0.7)
-        make = make_dense if kind == "dense" else make_fp8_dense
-        w = make(B, S, H, lens, causal=causal, seed=seed, device=DEV, out_dtype=out_dtype)
-        desc = f"{kind} B={B} S={S} H={H} out={out_dtype} causal={causal} lens={lens[:6]}"
-    else:
-        pool = int(r.choice([256, 512, 1024]))
-        topk = int(r.choice(EDGE[1:]) if r.random() < 0.3 else r.integers(1, min(pool, 700) + 1))
-        inv = float(r.choice([0.0, 0.05, 0.2]))
-        if kind in ("sparse", "sparse_fp8"):
-            w = make_sparse(B, S, H, pool_tokens_per_seq=pool, topk=topk, invalid_frac=inv, seed=seed, device=DEV,
-                            out_dtype=out_dtype, kv_format="fp8" if kind == "sparse_fp8" else "bf16")
-        else:
-            make = make_v41_sparse if kind == "v41" else make_fp4_sparse
-            w = make(B, S, H, pool_tokens_per_seq=pool, topk=topk, invalid_frac=inv, seed=seed, device=DEV)
-            w.out_dtype = out_dtype
-        if r.random() < 0.4:
-            tl = torch.as_tensor(r.integers(0, topk + 1, size=(B, S)), dtype=torch.int32)
-            w.topk_length = tl.to(DEV)
-        desc = f"{kind} B={B} S={S} H={H} out={out_dtype} pool={pool} topk={topk} invalid={inv}"
-    if r.random() < 0.3:
-        s = torch.as_tensor(r.normal(8.0, 4.0, size=H), dtype=torch.float32)
-        s[0] = -float("inf")
-        w.attn_sink = s.to(DEV)
-        desc += " sink"
-    return kind, w, desc
 
 
 def _run(w, num_cus, step):
@@ -88,7 +49,7 @@ def _run(w, num_cus, step):
 
 @pytest.mark.parametrize("seed", range(64))
 def test_random_problem(seed):
-    kind, w, desc = _draw(seed)
+    kind, w, desc = draw_random_problem(seed, DEV)
     print(desc, flush=True)
     num_cus = (0, 7, 64)[seed % 3]
     so, sl = _run(w, num_cus, step=True)
@@ -210,3 +171,19 @@ def test_random_combine(seed):
         assert np.array_equal(np.isneginf(gl[b, :, i]), np.isneginf(rl)), f"item {j}: lse -inf"
         fin = np.isfinite(rl)
         assert np.all(np.abs(gl[b, fin, i] - rl[fin]) < 1e-4), f"item {j}: lse"
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_random_problem_debug_mode(seed, monkeypatch):
+    """MLA_DEBUG=1 validates every call's inputs on the host first; valid
+    random problems must pass those checks and give the same outputs, bit for
+    bit, as without them."""
+    kind, w, desc = draw_random_problem(seed, DEV)
+    print(desc, flush=True)
+    ref = [_run(w, 0, step) for step in (True, False)]
+    monkeypatch.setenv("MLA_DEBUG", "1")
+    got = [_run(w, 0, step) for step in (True, False)]
+    monkeypatch.delenv("MLA_DEBUG")
+    for (ro, rl), (go, gl) in zip(ref, got):
+        as_bits = torch.int16 if ro.dtype == torch.bfloat16 else torch.int32
+        assert torch.equal(go.view(as_bits), ro.view(as_bits)) and torch.equal(gl.view(torch.int32), rl.view(torch.int32))

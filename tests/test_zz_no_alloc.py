@@ -10,7 +10,7 @@ import pytest
 import torch
 
 from workloads import make_dense, make_sparse
-from helpers import oracle, compare
+from helpers import draw_random_problem, oracle, compare
 
 pytestmark = pytest.mark.gpu
 
@@ -55,3 +55,12 @@ def test_noalloc_matches_the_step_on_two_calls(kind):
     out, lse = _both(small)
     ro, rl = oracle(small)
     compare(out.float().cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64), ro, rl)
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_noalloc_matches_the_step_on_random_problems(seed):
+    """Seeded random problems of every cache format (the generator the other
+    random tests use): the call that allocates nothing equals the step."""
+    kind, w, desc = draw_random_problem(seed, DEV)
+    print(f"noalloc random {desc}", flush=True)
+    _both(w)
