@@ -187,3 +187,29 @@ def test_random_problem_debug_mode(seed, monkeypatch):
     for (ro, rl), (go, gl) in zip(ref, got):
         as_bits = torch.int16 if ro.dtype == torch.bfloat16 else torch.int32
         assert torch.equal(go.view(as_bits), ro.view(as_bits)) and torch.equal(gl.view(torch.int32), rl.view(torch.int32))
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_random_problem_nan_in_q(seed):
+    """A NaN planted in one head of one query token of a random problem: that
+    head's output and lse are NaN exactly where the oracle's are (all of them
+    when the token sees anything, out 0 and lse -inf when it sees nothing), with
+    or without a sink, and every other value matches as before."""
+    kind, w, desc = draw_random_problem(seed, DEV)
+    r = np.random.default_rng(6000 + seed)
+    b, i, h = int(r.integers(0, w.batch)), int(r.integers(0, w.s_q)), int(r.integers(0, w.h_q))
+    w.q[b, i, h, int(r.integers(0, w.q.shape[-1]))] = float("nan")
+    print(f"{desc}; NaN in q[{b}, {i}, {h}]", flush=True)
+    kv = w.kv.cpu().numpy().reshape(-1, int(w.kv.shape[-1])) if kind in ("v41", "fp4") else None
+    ro, rl = oracle(w, kv=kv)
+    kw = dict(rel_l2=FP8_REL_L2, max_abs=1e-2) if kind in ("fp8", "sparse_fp8") else {}
+    for step in (True, False):
+        go, gl = _run(w, (0, 7)[seed % 2], step)
+        go = go.float().cpu().numpy().astype(np.float64)
+        gl = gl.cpu().numpy().astype(np.float64)
+        assert np.array_equal(np.isnan(go), np.isnan(ro)), "NaN positions of out differ"
+        assert np.array_equal(np.isnan(gl), np.isnan(rl)), "NaN positions of lse differ"
+        go2, ro2, gl2, rl2 = go.copy(), ro.copy(), gl.copy(), rl.copy()
+        go2[np.isnan(go2)] = ro2[np.isnan(ro2)] = 0.0
+        gl2[np.isnan(gl2)] = rl2[np.isnan(rl2)] = 0.0
+        print(step, compare(go2, gl2, ro2, rl2, **kw), flush=True)
