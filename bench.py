@@ -356,7 +356,7 @@ def bench_decode(args):
     w = load_workload(args.workload, dev)
     metric, cfg, bound = describe(args.workload, w)
     acct = flops_and_bytes(w)
-    dec = mla.Decoder.for_workload(w, dev)
+    dec = mla.Decoder.for_workload(w, dev, rescale_threshold=args.rescale_threshold)
     stream = torch.cuda.current_stream(dev)
     seqlens = None if w.topk else w.cache_seqlens
 
@@ -435,6 +435,8 @@ def bench_decode(args):
         "roofline_other": {"bound": "mfma" if bound == "hbm" else "hbm", **other},
         "decode_call_us": round(ms_decode * 1e3, 2),
     }
+    if args.rescale_threshold:
+        line["rescale_threshold"] = args.rescale_threshold
     del graph
     if scratch is not None:
         del scratch
@@ -523,6 +525,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-peaks", action="store_true", help="skip the measured copy / matmul peaks")
     ap.add_argument("--cold", action="store_true", help="write 512 MiB of scratch before every timed step")
+    ap.add_argument("--rescale-threshold", type=float, default=0.0,
+                    help="lazy rescale: raise a row's running max only past this many log2 units (0: the exact max)")
     ap.add_argument("--workload", default="dense_b64_s4096", choices=WORKLOADS,
                     help="dense_b64_s4096 (= config2) is the headline line; see the module docstring")
     ap.add_argument("--calibrate-copy", action="store_true",
