@@ -66,6 +66,10 @@ def test_plan_host_only():
     assert m.num_head_blocks == 1 and m.num_partitions == 256
     m = mla.plan(_problem(h_q=192, topk=2048), num_cus=256)
     assert m.num_head_blocks == 2 and m.num_partitions == 128
+    # the largest batches: 16384 query groups in all
+    for kw in (dict(batch=16384), dict(batch=8192, s_q=2), dict(batch=4096, s_q=4, topk=64)):
+        m = mla.plan(_problem(**kw), num_cus=256)
+        assert m.bytes == (8 + 5 * m.num_partitions + 16384 + 1) * 4
     for tau in (0.0, 6.0, 8.0, 30.0):   # lazy-rescale thresholds in range
         assert mla.plan(_problem(rescale_threshold=tau), num_cus=256).num_partitions == 128
 
@@ -86,7 +90,8 @@ def test_struct_layout_matches_header():
 @pytest.mark.parametrize("kw,status", [
     (dict(batch=0), 1), (dict(s_q=0), 1), (dict(h_q=0), 1), (dict(num_blocks=0), 1),
     (dict(max_blocks_per_seq=0), 1), (dict(topk=-1), 1), (dict(softmax_scale=float("nan")), 1), (dict(softmax_scale=0.0), 1), (dict(softmax_scale=-0.5), 1),
-    (dict(topk=64, causal=True), 2), (dict(batch=20000), 2),
+    (dict(topk=64, causal=True), 2), (dict(batch=20000), 2), (dict(batch=16385), 2), (dict(batch=8193, s_q=2), 2),
+    (dict(batch=4097, s_q=4, topk=64), 2),
     (dict(rescale_threshold=-1.0), 1), (dict(rescale_threshold=30.5), 1), (dict(rescale_threshold=float("nan")), 1),
     (dict(rescale_threshold=float("inf")), 1),
 ])
