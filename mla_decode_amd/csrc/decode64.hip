@@ -28,15 +28,17 @@
 //                       it is rescaled by alpha (skipped when no head's max
 //                       rose), so the multiplies of one block overlap the MFMAs
 //                       of the previous one.
-//   copy waves (6, 7)   stage tiles global -> LDS with 16-byte buffer loads
-//                       that write LDS directly (tokens past the valid count
-//                       fall outside the buffer range and land as zeros), and
-//                       publish each tile's valid token count.
+//   copy waves (6, 7)   stage tiles global -> registers -> LDS: 16-byte
+//                       buffer loads two steps ahead into one of two register
+//                       sets (tokens past the valid count fall outside the
+//                       buffer range and load as zeros), ds_write_b128 when
+//                       the tile's LDS buffer is free, and publish each tile's
+//                       valid token count.
 //
 // Step k (one workgroup barrier per step, LDS ring of four 32-token tiles):
 //   QK waves     softmax(k) and QK(k+1)        reads tile k+1
 //   PV waves     rescale and PV(k-1)           reads tile k-1
-//   copy waves   copy of tile k+2              writes the buffer of tile k-2
+//   copy waves   write tile k+2, load tile k+4  writes the buffer of tile k-2
 // so every SIMD has MFMA and vector work from two waves at once.
 //
 // Items whose KV range sits in one partition write out/lse directly; split
@@ -71,7 +73,6 @@ struct __attribute__((aligned(16))) Smem64 {
     int valid[kRing];               // valid tokens of the tile in each buffer
     int seg[2];                     // the current segment's output slot and (split count == 1)
     int pad[2];
-    unsigned char pf_sink[256];     // destination of the L2 prefetch loads (never read)
     unsigned char tile[kRing][kTileB];   // 32-token tiles (bf16, swizzled columns, see lds_chunk)
 };
 
@@ -104,34 +105,6 @@ __device__ __forceinline__ int lane_id64() {
     unsigned m = ~0u;
     __asm__ volatile("" : "+s"(m));
     return (int)__builtin_amdgcn_mbcnt_hi(m, __builtin_amdgcn_mbcnt_lo(m, 0u));
-}
-
-__device__ __forceinline__ i32x4 rsrc(const void* base, int num_records) {
-    const uint64_t p = (uint64_t)base;
-    i32x4 r;
-    r[0] = (int)(uint32_t)p;
-    r[1] = (int)((uint32_t)(p >> 32) & 0xffffu);
-    r[2] = num_records;
-    r[3] = 0x00020000;
-    return r;
-}
-
-// 16-byte-per-lane global -> LDS copy (one wave instruction writes 1 KiB of
-// LDS at M0 + offset + 16 lane; the immediate offset moves the global source
-// as well, so M0 is the destination minus the immediate).  Issued through
-// inline assembly so that the compiler does not wait for it before unrelated
-// LDS reads; the issuing wave waits with vmcnt before the step barrier.
-template <int IMM>
-__device__ __forceinline__ void copy_x4(const i32x4& rs, int voff, int lds) {
-    __asm__ volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen offset:%3 lds"
-                     :: "s"(lds - IMM), "v"(voff), "s"(rs), "i"(IMM) : "memory", "m0");
-}
-
-// 4-byte-per-lane global -> LDS load into a 256-byte sink: brings the source
-// lines into L2 ahead of their copy; nothing reads the sink
-__device__ __forceinline__ void prefetch_x1(const i32x4& rs, int voff, int lds) {
-    __asm__ volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, 0 offen lds"
-                     :: "s"(lds), "v"(voff), "s"(rs) : "memory", "m0");
 }
 
 __device__ __forceinline__ void barrier_only() {
@@ -220,7 +193,6 @@ __global__ void __launch_bounds__(kT, 1) decode64_kernel(const DecodeArgs a) {
     const unsigned char* kv = (const unsigned char*)a.kv;
     RowResolver rr{a.block_table, a.cache_seqlens, nullptr, a.s_q, a.max_blocks, 0, a.causal, a.num_rows};
 
-    const int lds_tiles = (int)(size_t)(lds_void_t*)&sm.tile[0][0];
 
     // One segment = the tiles of item j that this partition holds.  Every role
     // walks the same segments and passes the same barriers (n + 6 per segment).
@@ -290,77 +262,91 @@ __global__ void __launch_bounds__(kT, 1) decode64_kernel(const DecodeArgs a) {
             // token 8 tg + l / 8, column 8 cg + ((l % 8) ^ swz(token)); the byte
             // count of the buffer of token group tg stops at the valid tokens,
             // so the rest land as zeros.
-            auto copy_tile = [&](int it) __attribute__((always_inline)) {
+            // The 18 blocks of a tile are loaded into registers two steps before
+            // they are written to LDS (ds_write_b128 to the address a direct copy
+            // would fill), so each tile has two steps to arrive from HBM and two
+            // tiles are in flight per workgroup; tile it uses register set it % 2.
+            i32x4 st[2][18];
+            int nvs[2] = {0, 0};
+            const int ln = lane_id64();
+            const int tq = ln >> 3, sl = ln & 7;
+            const int fbe = tq * kRowBytes + 16 * (sl ^ tq);         // even token groups: swz = tq
+            const int fbo = tq * kRowBytes + 16 * (sl ^ tq ^ 1);     // odd token groups: swz = tq ^ 1
+            auto load_tile = [&](auto s_c, int it) __attribute__((always_inline)) {
+                constexpr int S = decltype(s_c)::value;
                 const int g = sg.g0 + it;
                 if (((g >> 1) - pt_base) >= 64) load_pages(g >> 1);
                 const int page = __builtin_amdgcn_readlane(pt_v, (g >> 1) - pt_base);
                 const bool ok = page_ok(page, a.num_rows);
                 int nvalid = min(sg.nslots - g * kSubTok, kSubTok);
                 if (!ok || nvalid < 0) nvalid = 0;
+                nvs[S] = nvalid;
                 const unsigned char* base = kv + (ok ? (int64_t)page * kTileBytes + (g & 1) * kTileB : 0);
-                const int dst = lds_tiles + ring_offset(it % kRing);
-                const int ln = lane_id64();
-                const int tq = ln >> 3, sl = ln & 7;
-                const int fbe = tq * kRowBytes + 16 * (sl ^ tq);         // even token groups: swz = tq
-                const int fbo = tq * kRowBytes + 16 * (sl ^ tq ^ 1);     // odd token groups: swz = tq ^ 1
                 unroll<0, 2>([&](auto u_c) __attribute__((always_inline)) {
                     constexpr int u = decltype(u_c)::value;
                     const int tg = 2 * cw + u;
-                    i32x4 rs = rsrc(base + 8 * tg * kRowBytes, min(max(nvalid - 8 * tg, 0), 8) * kRowBytes);
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) rs[e] = __builtin_amdgcn_readfirstlane(rs[e]);   // uniform by construction
+                    // base and byte count are uniform by construction; readfirstlane
+                    // lets the compiler see it (no per-lane descriptor loop)
+                    const uint64_t pb = (uint64_t)(base + 8 * tg * kRowBytes);
+                    const uint64_t pu = ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(pb >> 32)) << 32) |
+                                        (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)pb);
+                    const int nr = __builtin_amdgcn_readfirstlane(min(max(nvalid - 8 * tg, 0), 8) * kRowBytes);
+                    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void*)pu, 0, nr, 0x00020000);
                     unroll<0, 9>([&](auto cg_c) __attribute__((always_inline)) {
                         constexpr int cg = decltype(cg_c)::value;
-                        copy_x4<128 * cg>(rs, u ? fbo : fbe, dst + 1024 * (4 * cg + tg));
+                        st[S][9 * u + cg] = __builtin_bit_cast(
+                            i32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, (u ? fbo : fbe) + 128 * cg, 0, 0));
                     });
                 });
-                if (cw == 0) sm.valid[it % kRing] = nvalid;
             };
-            // L2 prefetch of tile it: one 4-byte load per 128-byte line (lines
-            // 144 cw .. 144 cw + 143 of the 288) into a sink in LDS that nothing
-            // reads.  Always three instructions, issued after a step's copies, so
-            // that the wait for those copies is vmcnt(3) (loads complete in issue
-            // order) and a prefetch has a whole step to arrive.
-            const int sink = (int)(size_t)(lds_void_t*)&sm.pf_sink[0];
-            auto prefetch_tile = [&](int it) __attribute__((always_inline)) {
-                const int g = sg.g0 + it;
-                int nbytes = 0;
-                const unsigned char* base = kv;
-                // a page past the window of page ids is not prefetched: the
-                // window is moved only by the copies, which still need it
-                if (it < sg.n && ((g >> 1) - pt_base) < 64) {
-                    const int page = __builtin_amdgcn_readlane(pt_v, (g >> 1) - pt_base);
-                    if (page_ok(page, a.num_rows)) {
-                        nbytes = max(0, min(sg.nslots - g * kSubTok, kSubTok)) * kRowBytes;
-                        base = kv + (int64_t)page * kTileBytes + (g & 1) * kTileB;
-                    }
-                }
-                const int lo = 128 * (144 * cw + lane_id64());
-                const int hi = 144 * 128 * (cw + 1);       // this wave's lines end here
-                i32x4 rs = rsrc(base, min(nbytes, hi));
-#pragma unroll
-                for (int e = 0; e < 4; ++e) rs[e] = __builtin_amdgcn_readfirstlane(rs[e]);   // uniform by construction
-                prefetch_x1(rs, lo, sink);
-                prefetch_x1(rs, lo + 8192, sink);
-                prefetch_x1(rs, lo + 16384, sink);
+            auto write_tile = [&](auto s_c, int it) __attribute__((always_inline)) {
+                constexpr int S = decltype(s_c)::value;
+                unsigned char* dst = sm.tile[0] + ring_offset(it % kRing) + 16 * ln;
+                unroll<0, 2>([&](auto u_c) __attribute__((always_inline)) {
+                    constexpr int u = decltype(u_c)::value;
+                    const int tg = 2 * cw + u;
+                    unroll<0, 9>([&](auto cg_c) __attribute__((always_inline)) {
+                        constexpr int cg = decltype(cg_c)::value;
+                        *(i32x4*)(dst + 1024 * (4 * cg + tg)) = st[S][9 * u + cg];
+                    });
+                });
+                if (cw == 0) sm.valid[it % kRing] = nvs[S];
             };
-            constexpr int kLead = 4;    // step k copies tile k + 2 and prefetches tile k + kLead
-            // tile 0 first: the L2 prefetches of tiles 1 and 2 wait until it has
-            // landed, so that they do not compete with it and with Q at launch
-            copy_tile(0);
-            __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): tile 0 has landed
-#pragma unroll
-            for (int it = 1; it < kLead - 1; ++it) prefetch_tile(it);
-            barrier_lds();
-            for (int k = -1; k <= sg.n; ++k) {
-                if (k + 2 < sg.n) {
-                    copy_tile(k + 2);
-                    prefetch_tile(k + kLead);
-                    __builtin_amdgcn_s_waitcnt(0x0F73);   // vmcnt(3): this wave's copies have landed
-                } else {
-                    __builtin_amdgcn_s_waitcnt(0x0F70);
-                }
+            // Step k writes tile k + 2 (set k % 2) and loads tile k + 4 into the
+            // same set.  The steps that load (k + 4 < n) run in a loop of their
+            // own, unrolled by two, so that the loads are unconditional there and
+            // the compiler's waits before the writes leave the newer set in flight.
+            auto step_load = [&](auto s_c, int k) __attribute__((always_inline)) {
+                write_tile(s_c, k + 2);
+                load_tile(s_c, k + 4);
                 barrier_lds();
+            };
+            auto step_tail = [&](auto s_c, int k) __attribute__((always_inline)) {
+                if (k + 2 < sg.n) write_tile(s_c, k + 2);
+                barrier_lds();
+            };
+            load_tile(Int<0>{}, 0);
+            if (1 < sg.n) load_tile(Int<1>{}, 1);
+            write_tile(Int<0>{}, 0);
+            if (2 < sg.n) load_tile(Int<0>{}, 2);
+            barrier_lds();   // tile 0 has landed
+            int k = -1;
+            for (; k + 5 < sg.n; k += 2) {   // steps k and k + 1 both load
+                step_load(Int<1>{}, k);
+                step_load(Int<0>{}, k + 1);
+            }
+            if (k + 4 < sg.n) {              // one more loading step (set 1)
+                step_load(Int<1>{}, k);
+                ++k;
+                for (; k <= sg.n; k += 2) {
+                    step_tail(Int<0>{}, k);
+                    if (k + 1 <= sg.n) step_tail(Int<1>{}, k + 1);
+                }
+            } else {
+                for (; k <= sg.n; k += 2) {
+                    step_tail(Int<1>{}, k);
+                    if (k + 1 <= sg.n) step_tail(Int<0>{}, k + 1);
+                }
             }
             __builtin_amdgcn_s_waitcnt(0x0F70);   // every load of this wave has written LDS
             barrier_lds();   // epilogue
