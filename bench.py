@@ -49,8 +49,15 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 MFMA_BF16_PEAK_TFLOPS = 2516.6  # MI355X dense bf16 MFMA, published (256 CU x 2.4 GHz x 4096)
 METRIC = "MLA decode TFLOPS + HBM GB/s, µs/step at b=64,h_q=128,seqlen=4096 (1 GPU)"
-KERNEL_SOURCES = ("mla_decode_amd/csrc/decode.hip", "mla_decode_amd/csrc/decode64.hip",
-                  "mla_decode_amd/csrc/common.h")
+# sources of the partial-attention kernel a workload runs: the 64-head dense
+# kernel for a bf16 cache without top-k, the 128-head kernel otherwise
+KERNEL_SOURCES = {
+    "decode64": ("mla_decode_amd/csrc/decode64.hip", "mla_decode_amd/csrc/common.h",
+                 "mla_decode_amd/csrc/wave_sched.h"),
+    "decode": ("mla_decode_amd/csrc/decode.hip", "mla_decode_amd/csrc/common.h",
+               "mla_decode_amd/csrc/wave_sched.h"),
+}
+DECODE64_WORKLOADS = ("dense_b64_s4096", "config1", "config2", "config3")
 WARMUP_MIN_S = 0.1
 
 # workload -> (counter summary file, roofline bound)
@@ -70,9 +77,10 @@ BOUND = {"config1": "hbm", "config2": "hbm", "dense_b64_s4096": "hbm", "config3"
          "config5": "mfma"}
 
 
-def kernel_source_hash():
+def kernel_source_hash(workload):
+    """Hash of the source files of the partial-attention kernel ``workload`` runs."""
     h = hashlib.sha256()
-    for f in KERNEL_SOURCES:
+    for f in KERNEL_SOURCES["decode64" if workload in DECODE64_WORKLOADS else "decode"]:
         p = os.path.join(ROOT, f)
         if os.path.exists(p):
             with open(p, "rb") as fh:
@@ -92,7 +100,7 @@ def measured_traffic(workload):
             c = json.load(f)
     except (OSError, ValueError):
         return None
-    if c.get("kernel_source_sha") != kernel_source_hash():
+    if c.get("kernel_source_sha") != kernel_source_hash(workload):
         return None
     return c.get("hbm_bytes_per_launch")
 
