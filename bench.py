@@ -393,7 +393,15 @@ def bench_decode(args):
                        ref_out.view(torch.int16 if ref_out.dtype == torch.bfloat16 else torch.int32)) \
         and torch.equal(dec.lse, ref_lse), "graph replay differs from the eager step"
     _warmup(graph.replay, 10, 0.02)
-    ms_graph, _ = _timed(graph.replay, args.steps, stream, before)
+    # eager and graph steps in alternating blocks, so both see the same clock
+    # (the chip slows as it heats, and a block timed later would look slower)
+    blk = max(args.steps // 4, 5)
+    eager_blocks, graph_blocks = [], []
+    for _ in range(4):
+        eager_blocks.append(_timed(step, blk, stream, before)[0])
+        graph_blocks.append(_timed(graph.replay, blk, stream, before)[0])
+    ms_graph = sum(graph_blocks) / len(graph_blocks)
+    ms_eager_inter = sum(eager_blocks) / len(eager_blocks)
 
     ms_decode, _ = _timed(lambda: dec.decode(w.q, w.kv, w.block_table, w.cache_seqlens, w.indices, stream),
                           args.steps, stream, before)
@@ -431,6 +439,8 @@ def bench_decode(args):
         "us_p50": round(_pct(per_step, 50) * 1e3, 2),
         "us_p90": round(_pct(per_step, 90) * 1e3, 2),
         "graph_us_per_step": round(ms_graph * 1e3, 2),
+        "graph_vs_eager": {"graph_us": round(ms_graph * 1e3, 2), "eager_us": round(ms_eager_inter * 1e3, 2),
+                           "how": f"4 alternating blocks of {blk} eager and {blk} graph-replayed steps"},
         "hbm_gbs": round(nbytes / (ms_step * 1e-3) / 1e9, 1),
         "higher_is_better": True,
         "scaling": "weak",
