@@ -57,7 +57,7 @@ KERNEL_SOURCES = {
     "decode": ("mla_decode_amd/csrc/decode.hip", "mla_decode_amd/csrc/common.h",
                "mla_decode_amd/csrc/wave_sched.h"),
 }
-DECODE64_WORKLOADS = ("dense_b64_s4096", "config1", "config2", "config3")
+DECODE64_WORKLOADS = ("dense_b64_s4096", "config1", "config2", "config3", "config4", "sparse_prefill")
 WARMUP_MIN_S = 0.1
 
 # workload -> (counter summary file, roofline bound)
@@ -65,13 +65,13 @@ COUNTER_FILES = {
     "dense_b64_s4096": "decode64_kernel_dense_b64_h128_s4096_counters.json",
     "config2": "decode64_kernel_dense_b64_h128_s4096_counters.json",
     "config3": "decode64_kernel_config3_b128_s2_causal_varlen_counters.json",
-    "config4": "decode_kernel_sparse_config4_b64_topk2048_counters.json",
+    "config4": "decode64_kernel_sparse_config4_b64_topk2048_counters.json",
     "config5": "decode_kernel_fp8_config5_b32_s16384_counters.json",
     "fp8_sparse_topk2048": "decode_kernel_fp8_sparse_b128_s2_h128_topk2048_counters.json",
     "fp8_sparse_topk32768": "decode_kernel_fp8_sparse_b128_s2_h128_topk32768_counters.json",
     "v41_sparse_topk2048": "decode_kernel_fp8_528_sparse_b128_s2_h128_topk2048_counters.json",
     "fp4_sparse_topk2048": "decode_kernel_fp4_sparse_b128_s2_h128_topk2048_counters.json",
-    "sparse_prefill": "decode_kernel_sparse_prefill_s4096_kv32768_topk2048_counters.json",
+    "sparse_prefill": "decode64_kernel_sparse_prefill_s4096_kv32768_topk2048_counters.json",
 }
 BOUND = {"config1": "hbm", "config2": "hbm", "dense_b64_s4096": "hbm", "config3": "mfma", "config4": "hbm",
          "config5": "mfma"}
@@ -342,12 +342,12 @@ def describe(name, w):
 
 def kernel_name(w):
     """The partial-attention kernel a workload runs (the library's dispatch rule)."""
-    if not w.topk and w.kv_format == "bf16":
-        fused = w.batch * w.s_q <= 256
-        return (f"decode64_kernel<{'true' if fused else 'false'}> (dense bf16 cache, 64 heads per workgroup"
+    fused = w.batch * w.s_q <= 256
+    if w.kv_format == "bf16" and (not w.topk or (w.num_blocks * 64 + 2) * 1152 < 1 << 32):
+        return (f"decode64_kernel<{'true' if fused else 'false'}, {'true' if w.topk else 'false'}> "
+                f"(bf16 cache, {'top-k rows' if w.topk else 'dense pages'}, 64 heads per workgroup"
                 + (", schedule computed in the kernel)" if fused else ")"))
     fmt = {"bf16": 0, "fp8": 1, "fp8_528": 2, "fp4_288": 3}[w.kv_format]
-    fused = w.batch * w.s_q <= 256
     # the third argument selects the dense instantiation that computes its own schedule
     dense_fused = "true" if not w.topk and fused else "false"
     return (f"decode_kernel<{'true' if w.topk else 'false'}, {fmt}, {dense_fused}> (128 heads per workgroup"

@@ -62,9 +62,15 @@ mla_status_t device_cus(int32_t* out) {
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
-// Dense decode over a bf16 cache runs the 64-heads-per-workgroup kernel; the
-// other formats and the sparse calls run the 128-heads-per-workgroup one.
-bool uses_decode64(const mla_problem_t* p) { return p->topk == 0 && p->kv_format == MLA_KV_BF16_576; }
+// Calls over a bf16 cache run the 64-heads-per-workgroup kernel: dense ones
+// always, top-k ones when every row offset of the cache, and one row past its
+// end, fits the 32-bit offsets of a buffer load (the kernel gathers rows
+// through one buffer over the whole cache).  The quantised formats and larger
+// top-k caches run the 128-heads-per-workgroup kernel.
+bool uses_decode64(const mla_problem_t* p) {
+    if (p->kv_format != MLA_KV_BF16_576) return false;
+    return p->topk == 0 || ((int64_t)p->num_blocks * kBlock + 2) * 1152 < ((int64_t)1 << 32);
+}
 int32_t heads_per_block(const mla_problem_t* p) { return uses_decode64(p) ? 64 : mla::kHeadsPerWG; }
 
 mla_status_t validate(const mla_problem_t* p) {

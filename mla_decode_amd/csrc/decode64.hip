@@ -1,5 +1,6 @@
-// Split-KV partial-attention kernel for absorbed-MLA decode on gfx950, dense
-// bf16 cache: 64 query heads per workgroup, waves split by role.
+// Split-KV partial-attention kernel for absorbed-MLA decode on gfx950, bf16
+// cache (dense pages or top-k rows): 64 query heads per workgroup, waves split
+// by role.
 //
 // A workgroup computes 64 heads of one scheduler partition (a contiguous run
 // of 32-token KV tiles, possibly spanning several items).  The two workgroups
@@ -30,10 +31,17 @@
 //                       of the previous one.
 //   copy waves (6, 7)   stage tiles global -> registers -> LDS: 16-byte
 //                       buffer loads two steps ahead into one of two register
-//                       sets (tokens past the valid count fall outside the
-//                       buffer range and load as zeros), ds_write_b128 when
-//                       the tile's LDS buffer is free, and publish each tile's
-//                       valid token count.
+//                       sets, ds_write_b128 when the tile's LDS buffer is
+//                       free, and publish which tokens of each tile are valid.
+//                       Dense: a page's tokens past the valid count fall
+//                       outside the buffer range and load as zeros; the count
+//                       is published.  Top-k: each lane loads its token's
+//                       index one step before the row (so the index wait
+//                       never waits on the tile in flight), rows are gathered
+//                       through one buffer over the whole cache, an invalid
+//                       entry (-1, out of range, past the item's top-k
+//                       length) reads past its end as zeros, and a 32-bit mask
+//                       of valid tokens is published.
 //
 // Step k (one workgroup barrier per step, LDS ring of four 32-token tiles):
 //   QK waves     softmax(k) and QK(k+1)        reads tile k+1
@@ -70,7 +78,8 @@ struct __attribute__((aligned(16))) Smem64 {
     float alpha[2][2][32];          // rescale factor of O for tile k [k & 1][head block][head]
     float fin_inv[kH];              // epilogue: output scale 1/l (times the sink factor)
     float fin_pad[kH];
-    int valid[kRing];               // valid tokens of the tile in each buffer
+    int valid[kRing];               // dense: valid tokens of the tile in each buffer
+    int vmask[kRing][2];            // top-k: valid-token bits of each buffer's tile [copy wave]
     int seg[2];                     // the current segment's output slot and (split count == 1)
     int pad[2];
     unsigned char tile[kRing][kTileB];   // 32-token tiles (bf16, swizzled columns, see lds_chunk)
@@ -136,7 +145,7 @@ __device__ __forceinline__ void unroll(F&& f) {
 
 }  // namespace
 
-template <bool FUSED>
+template <bool FUSED, bool SPARSE>
 __global__ void __launch_bounds__(kT, 1) decode64_kernel(const DecodeArgs a) {
     __shared__ Smem64 sm;
     const int tid = threadIdx.x;
@@ -179,7 +188,7 @@ __global__ void __launch_bounds__(kT, 1) decode64_kernel(const DecodeArgs a) {
     if constexpr (FUSED) {
         const int ln = (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
         fR = N <= 64 ? 1 : N <= 128 ? 2 : 4;
-        wave_schedule_any(a, a.cache_seqlens, N, part, ln, fR, ws);
+        wave_schedule_any(a, SPARSE ? a.topk_length : a.cache_seqlens, N, part, ln, fR, ws);
         jb = ws.jb; tbeg = ws.tbeg; je = ws.je; tend = ws.tend; slot0 = ws.slot0;
         // the schedule written back: each partition's record by its first head
         // block, header and split offsets by workgroup 0 (copy wave 0 of each)
@@ -191,7 +200,8 @@ __global__ void __launch_bounds__(kT, 1) decode64_kernel(const DecodeArgs a) {
     const int H = a.h_q;
     const float c = a.scale_log2;
     const unsigned char* kv = (const unsigned char*)a.kv;
-    RowResolver rr{a.block_table, a.cache_seqlens, nullptr, a.s_q, a.max_blocks, 0, a.causal, a.num_rows};
+    RowResolver rr{a.block_table, SPARSE ? a.topk_length : a.cache_seqlens, a.indices, a.s_q, a.max_blocks,
+                   SPARSE ? a.topk : 0, a.causal, a.num_rows};
 
 
     // One segment = the tiles of item j that this partition holds.  Every role
@@ -252,7 +262,7 @@ __global__ void __launch_bounds__(kT, 1) decode64_kernel(const DecodeArgs a) {
                 pt_v = pi < npages_item ? a.block_table[(int64_t)sg.b * a.max_blocks + pi] : 0;
                 __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
             };
-            load_pages(sg.g0 >> 1);
+            if constexpr (!SPARSE) load_pages(sg.g0 >> 1);
             // A tile is copied as 36 blocks of 1 KiB, block 4 cg + tg holding the
             // 128-byte line cg (columns 8 cg .. 8 cg + 7) of tokens 8 tg .. 8 tg + 7,
             // so that every copy instruction reads eight whole lines (see
@@ -272,8 +282,48 @@ __global__ void __launch_bounds__(kT, 1) decode64_kernel(const DecodeArgs a) {
             const int tq = ln >> 3, sl = ln & 7;
             const int fbe = tq * kRowBytes + 16 * (sl ^ tq);         // even token groups: swz = tq
             const int fbo = tq * kRowBytes + 16 * (sl ^ tq ^ 1);     // odd token groups: swz = tq ^ 1
+            // top-k: lane's token is slot 32 g + 8 tg + tq of the item; its
+            // index for tile it sits in ix[it % 2][u], loaded a step ahead
+            int ix[2][2] = {{-1, -1}, {-1, -1}};
+            int msk[2] = {0, 0};
+            const int64_t ibase = (int64_t)j * a.topk;
+            const uint32_t nrec = (uint32_t)a.num_rows * (uint32_t)kRowBytes;   // < 2^32 - 2 rows: host-checked
+            auto load_idx = [&](auto s_c, int it) __attribute__((always_inline)) {
+                constexpr int S = decltype(s_c)::value;
+                unroll<0, 2>([&](auto u_c) __attribute__((always_inline)) {
+                    constexpr int u = decltype(u_c)::value;
+                    const int slot = (sg.g0 + it) * kSubTok + 8 * (2 * cw + u) + tq;
+                    int v = -1;
+                    if (it < sg.n && slot < sg.nslots) v = a.indices[ibase + slot];
+                    ix[S][u] = v;
+                });
+            };
             auto load_tile = [&](auto s_c, int it) __attribute__((always_inline)) {
                 constexpr int S = decltype(s_c)::value;
+                if constexpr (SPARSE) {
+                    // one buffer over the whole cache; an invalid row's offset
+                    // starts at its end, so its 16-byte loads return zeros
+                    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void*)kv, 0, (int)nrec, 0x00020000);
+                    uint32_t m = 0;
+                    unroll<0, 2>([&](auto u_c) __attribute__((always_inline)) {
+                        constexpr int u = decltype(u_c)::value;
+                        const int64_t r = sparse_entry_row(ix[S][u], a.num_rows);
+                        const bool ok = r >= 0;
+                        const uint32_t vo = (ok ? (uint32_t)r * (uint32_t)kRowBytes : nrec) +
+                                            (uint32_t)(16 * (sl ^ tq ^ u));
+                        // token 8 tg + t is valid when lane 8 t of the group is
+                        const uint64_t bal = __builtin_amdgcn_ballot_w64(ok);
+#pragma unroll
+                        for (int t = 0; t < 8; ++t) m |= (uint32_t)((bal >> (8 * t)) & 1u) << (8 * (2 * cw + u) + t);
+                        unroll<0, 9>([&](auto cg_c) __attribute__((always_inline)) {
+                            constexpr int cg = decltype(cg_c)::value;
+                            st[S][9 * u + cg] = __builtin_bit_cast(
+                                i32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, (int)(vo + 128 * cg), 0, 0));
+                        });
+                    });
+                    msk[S] = (int)m;
+                    return;
+                }
                 const int g = sg.g0 + it;
                 if (((g >> 1) - pt_base) >= 64) load_pages(g >> 1);
                 const int page = __builtin_amdgcn_readlane(pt_v, (g >> 1) - pt_base);
@@ -310,14 +360,20 @@ __global__ void __launch_bounds__(kT, 1) decode64_kernel(const DecodeArgs a) {
                         *(i32x4*)(dst + 1024 * (4 * cg + tg)) = st[S][9 * u + cg];
                     });
                 });
-                if (cw == 0) sm.valid[it % kRing] = nvs[S];
+                if constexpr (SPARSE) sm.vmask[it % kRing][cw] = msk[S];
+                else if (cw == 0) sm.valid[it % kRing] = nvs[S];
             };
             // Step k writes tile k + 2 (set k % 2) and loads tile k + 4 into the
             // same set.  The steps that load (k + 4 < n) run in a loop of their
             // own, unrolled by two, so that the loads are unconditional there and
             // the compiler's waits before the writes leave the newer set in flight.
             auto step_load = [&](auto s_c, int k) __attribute__((always_inline)) {
+                constexpr int S = decltype(s_c)::value;
                 write_tile(s_c, k + 2);
+                // top-k: the index of tile k + 5 is requested before the rows of
+                // tile k + 4, so the next step's wait for it leaves those rows
+                // in flight
+                if constexpr (SPARSE) load_idx(Int<1 - S>{}, k + 5);
                 load_tile(s_c, k + 4);
                 barrier_lds();
             };
@@ -325,8 +381,17 @@ __global__ void __launch_bounds__(kT, 1) decode64_kernel(const DecodeArgs a) {
                 if (k + 2 < sg.n) write_tile(s_c, k + 2);
                 barrier_lds();
             };
-            load_tile(Int<0>{}, 0);
-            if (1 < sg.n) load_tile(Int<1>{}, 1);
+            if constexpr (SPARSE) {
+                load_idx(Int<0>{}, 0);
+                load_idx(Int<1>{}, 1);
+                load_tile(Int<0>{}, 0);
+                load_idx(Int<0>{}, 2);
+                if (1 < sg.n) load_tile(Int<1>{}, 1);
+                load_idx(Int<1>{}, 3);
+            } else {
+                load_tile(Int<0>{}, 0);
+                if (1 < sg.n) load_tile(Int<1>{}, 1);
+            }
             write_tile(Int<0>{}, 0);
             if (2 < sg.n) load_tile(Int<0>{}, 2);
             barrier_lds();   // tile 0 has landed
@@ -477,7 +542,17 @@ __global__ void __launch_bounds__(kT, 1) decode64_kernel(const DecodeArgs a) {
             auto scores = [&](int nv) __attribute__((always_inline)) {
 #pragma unroll
                 for (int r = 0; r < 16; ++r) s[r] = sa[r] + sb[r];
-                if (nv < kSubTok) {
+                if constexpr (SPARSE) {
+                    // nv: bit t set when token t of the tile is valid
+                    if (nv != -1) {
+                        const int h4 = 4 * (lane_id64() >> 5);
+#pragma unroll
+                        for (int r = 0; r < 16; ++r) {
+                            const int tok = 8 * (r >> 2) + h4 + (r & 3);
+                            if (!(((uint32_t)nv >> tok) & 1u)) s[r] = -INFINITY;
+                        }
+                    }
+                } else if (nv < kSubTok) {
                     const int h4 = 4 * (lane_id64() >> 5);
 #pragma unroll
                     for (int r = 0; r < 16; ++r) {
@@ -491,12 +566,17 @@ __global__ void __launch_bounds__(kT, 1) decode64_kernel(const DecodeArgs a) {
             // uses it at its end, so the read's latency is hidden.
             // step -1: QK(0)
             int nv_raw = 0;
-            qk(0, Int<0>{}, 0, [&] { nv_raw = sm.valid[0]; });
+            // a tile's validity: its token count (dense) or token bits (top-k)
+            auto valid_of = [&](int b) __attribute__((always_inline)) -> int {
+                if constexpr (SPARSE) return sm.vmask[b][0] | sm.vmask[b][1];
+                else return sm.valid[b];
+            };
+            qk(0, Int<0>{}, 0, [&] { nv_raw = valid_of(0); });
             int nv = __builtin_amdgcn_readfirstlane(nv_raw);
             barrier_lds();
             // steps 0 .. n-2: softmax(k) and QK(k+1)
             for (int k = 0; k + 1 < sg.n; ++k) {
-                qk(k + 1, Int<1>{}, k & 1, [&] { scores(nv); nv_raw = sm.valid[(k + 1) % kRing]; });
+                qk(k + 1, Int<1>{}, k & 1, [&] { scores(nv); nv_raw = valid_of((k + 1) % kRing); });
                 nv = __builtin_amdgcn_readfirstlane(nv_raw);
                 barrier_lds();
             }
@@ -725,8 +805,14 @@ __global__ void __launch_bounds__(kT, 1) decode64_kernel(const DecodeArgs a) {
 }
 
 hipError_t launch_decode64(const DecodeArgs& a, hipStream_t stream) {
-    if (a.fused) hipLaunchKernelGGL(decode64_kernel<true>, dim3(a.num_parts * a.n_hblk), dim3(kT), 0, stream, a);
-    else hipLaunchKernelGGL(decode64_kernel<false>, dim3(a.num_parts * a.n_hblk), dim3(kT), 0, stream, a);
+    const dim3 grid(a.num_parts * a.n_hblk), block(kT);
+    if (a.topk > 0) {
+        if (a.fused) hipLaunchKernelGGL((decode64_kernel<true, true>), grid, block, 0, stream, a);
+        else hipLaunchKernelGGL((decode64_kernel<false, true>), grid, block, 0, stream, a);
+    } else {
+        if (a.fused) hipLaunchKernelGGL((decode64_kernel<true, false>), grid, block, 0, stream, a);
+        else hipLaunchKernelGGL((decode64_kernel<false, false>), grid, block, 0, stream, a);
+    }
     return hipGetLastError();
 }
 

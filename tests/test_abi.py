@@ -61,10 +61,15 @@ def test_plan_host_only():
     assert m.num_head_blocks == 3 and m.num_partitions == 85
     m = mla.plan(_problem(h_q=16, batch=2, num_blocks=8, max_blocks_per_seq=4), num_cus=256)
     assert m.num_head_blocks == 1 and m.num_partitions == 256
-    # other formats and top-k problems: 128 heads per workgroup
+    # top-k over a bf16 cache whose row offsets fit 32 bits: 64 heads per workgroup
+    m = mla.plan(_problem(h_q=192, topk=2048), num_cus=256)
+    assert m.num_head_blocks == 3 and m.num_partitions == 85
+    # quantised formats and larger bf16 top-k caches: 128 heads per workgroup
     m = mla.plan(_problem(kv_format="fp8"), num_cus=256)
     assert m.num_head_blocks == 1 and m.num_partitions == 256
-    m = mla.plan(_problem(h_q=192, topk=2048), num_cus=256)
+    m = mla.plan(_problem(h_q=192, topk=2048, num_blocks=58254), num_cus=256)   # (64 n + 2) 1152 < 2^32
+    assert m.num_head_blocks == 3
+    m = mla.plan(_problem(h_q=192, topk=2048, num_blocks=58255), num_cus=256)
     assert m.num_head_blocks == 2 and m.num_partitions == 128
     # the largest batches: 16384 query groups in all
     for kw in (dict(batch=16384), dict(batch=8192, s_q=2), dict(batch=4096, s_q=4, topk=64)):
