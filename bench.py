@@ -518,7 +518,10 @@ def bench_prefill(args):
                                "top-k 2048 of each row's visible rows, 128 heads, N(0,1) inputs",
                    "s_q": s_q, "s_kv": s_kv, "h_q": h_q, "topk": topk, "d_qk": 576, "d_v": 512,
                    "step": "metadata + sparse prefill (partial + combine when needed)"},
-        "roofline": {"bound": "mfma", "kernel": "decode_kernel<true, 0> (128 heads per workgroup)",
+        "roofline": {"bound": "mfma",
+                     "kernel": kernel_name(types.SimpleNamespace(kv_format="bf16", topk=topk, batch=1, s_q=s_q,
+                                                                 num_blocks=p.num_blocks)),
+                     "algorithmic_bytes_per_launch": nbytes,
                      "achieved": round(kern_tflops, 1), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(kern_tflops / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": measured_traffic("sparse_prefill"),
                      "algorithmic_flops": flops, "us_per_launch": round(ms_kernel * 1e3, 2)},
